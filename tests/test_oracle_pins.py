@@ -1,0 +1,529 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each check below would fail for a plausible slip in the oracle: a wrong
+codebook scale or level, a transposed or re-ordered transform, a wrong sign,
+a dropped norm, an off-by-one code, a wrong bit order, a wrong GQA mapping, a
+wrong softmax scale, a k-means update error.  Independent routes used:
+closed forms, the published Gaussian Lloyd-Max table (tests/golden), numerical
+quadrature (scipy), scipy's Sylvester Hadamard matrix, numpy bit unpacking,
+torch's scaled-dot-product attention on dequantized keys, scikit-learn's Lloyd
+k-means, and brute-force nearest-level / nearest-centroid search.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.integrate
+import scipy.linalg
+import scipy.stats
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "max1960_gaussian_lloyd_max.txt")
+
+
+def _max_table():
+    tab = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            tab[(int(parts[0]), parts[1])] = [p for p in parts[2:]]
+    return tab
+
+
+def _tol(s: str) -> float:
+    # half a unit in the last printed digit, plus slack for known last-digit errors in the table
+    dec = len(s.split(".")[1]) if "." in s else 0
+    return 0.5 * 10.0 ** (-dec) + 1.5e-4
+
+
+# ----------------------------------------------------------------------------------------------
+# Codebook
+# ----------------------------------------------------------------------------------------------
+
+def test_lloyd_max_b1_closed_form(oracle_mod):
+    c, t, it = oracle_mod.lloyd_max_unit(1)
+    assert it > 0
+    assert c[1] == pytest.approx(math.sqrt(2.0 / math.pi), abs=1e-12)
+    assert c[0] == -c[1]
+    assert t[0] == 0.0
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_lloyd_max_matches_max_1960_table(oracle_mod, b):
+    L = 1 << b
+    tab = _max_table()
+    c, t, it = oracle_mod.lloyd_max_unit(b)
+    assert it > 0
+    pos_levels = c[L // 2:]
+    pos_thr = t[L // 2 - 1:]
+    for got, s in zip(pos_levels, tab[(L, "levels")]):
+        assert abs(got - float(s)) <= _tol(s), (b, got, s)
+    for got, s in zip(pos_thr, tab[(L, "thresholds")]):
+        assert abs(got - float(s)) <= _tol(s), (b, got, s)
+    mse = oracle_mod.quantizer_mse_unit(b, c, t)
+    assert mse == pytest.approx(float(tab[(L, "mse")][0]), rel=1e-3)
+
+
+def test_lloyd_max_b2_values_given_for_the_method(oracle_mod):
+    c, _, _ = oracle_mod.lloyd_max_unit(2)
+    assert c[2] == pytest.approx(0.4528, abs=5e-5)
+    assert c[3] == pytest.approx(1.5104, abs=5e-5)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_lloyd_max_fixed_point_by_quadrature(oracle_mod, b):
+    """Every level is the conditional mean of its cell (scipy quadrature, independent of erfc)."""
+    L = 1 << b
+    c, t, _ = oracle_mod.lloyd_max_unit(b)
+    edges = [-np.inf] + list(t) + [np.inf]
+    pdf = scipy.stats.norm.pdf
+    for j in range(L):
+        mass = scipy.integrate.quad(pdf, edges[j], edges[j + 1], epsabs=1e-14, epsrel=1e-13)[0]
+        mom = scipy.integrate.quad(lambda x: x * pdf(x), edges[j], edges[j + 1], epsabs=1e-14, epsrel=1e-13)[0]
+        assert mom / mass == pytest.approx(c[j], abs=1e-10)
+    # thresholds are midpoints, levels strictly increasing and odd-symmetric
+    np.testing.assert_allclose(t, 0.5 * (c[1:] + c[:-1]), rtol=0, atol=1e-15)
+    assert np.all(np.diff(c) > 0)
+    np.testing.assert_array_equal(c, -c[::-1])
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_lloyd_max_is_a_local_minimum_of_mse(oracle_mod, b):
+    """Perturbing any single level (thresholds re-derived) raises the quadrature MSE."""
+    c, t, _ = oracle_mod.lloyd_max_unit(b)
+
+    def mse_quad(levels):
+        thr = 0.5 * (levels[1:] + levels[:-1])
+        edges = [-np.inf] + list(thr) + [np.inf]
+        tot = 0.0
+        for j, cj in enumerate(levels):
+            tot += scipy.integrate.quad(lambda x: (x - cj) ** 2 * scipy.stats.norm.pdf(x),
+                                        edges[j], edges[j + 1], epsabs=1e-14)[0]
+        return tot
+
+    base = mse_quad(c)
+    assert base == pytest.approx(oracle_mod.quantizer_mse_unit(b, c, t), rel=1e-9)
+    for j in range(len(c)):
+        for eps in (1e-3, -1e-3):
+            p = c.copy()
+            p[j] += eps
+            assert mse_quad(p) > base
+
+
+@pytest.mark.parametrize("d,b", [(16, 2), (64, 4), (128, 3), (128, 1)])
+def test_codebook_is_unit_quantizer_over_sqrt_d(oracle_mod, d, b):
+    c, t, _ = oracle_mod.lloyd_max_unit(b)
+    lv, th = oracle_mod.codebook(d, b)
+    np.testing.assert_allclose(lv, c / math.sqrt(d), rtol=1e-15)
+    np.testing.assert_allclose(th, t / math.sqrt(d), rtol=1e-15)
+
+
+def test_rotated_coordinates_have_variance_one_over_d(oracle_mod):
+    """The premise of the fixed codebook: coordinates of H D k/|k| spread like N(0, 1/d)."""
+    d = 64
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((2000, d)) * rng.lognormal(0, 1, size=d)  # outlier channels
+    s = W.signs(W.LONGCTX)
+    lv, th = oracle_mod.codebook(d, 4)
+    _, _, y, _ = oracle_mod.encode_keys(th, s, k, 4)
+    assert np.mean(y ** 2) == pytest.approx(1.0 / d, rel=1e-12)  # exact: |y| = 1
+    # the rotation pulls outlier channels towards the Gaussian shape
+    kurt = np.mean(y ** 4) / np.mean(y ** 2) ** 2
+    raw = k / np.linalg.norm(k, axis=1, keepdims=True)
+    kurt_raw = np.mean(raw ** 4) / np.mean(raw ** 2) ** 2
+    assert abs(kurt - 3.0) < 1.0 < abs(kurt_raw - 3.0)
+    # isotropic keys: a coordinate of a uniform unit vector has kurtosis 3d/(d+2) (closed form)
+    k_iso = rng.standard_normal((20000, d))
+    _, _, y_iso, _ = oracle_mod.encode_keys(th, s, k_iso, 4)
+    kurt_iso = np.mean(y_iso ** 4) / np.mean(y_iso ** 2) ** 2
+    assert kurt_iso == pytest.approx(3.0 * d / (d + 2), rel=0.02)
+
+
+# ----------------------------------------------------------------------------------------------
+# Transform
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256])
+def test_hadamard_is_sylvester_and_orthogonal(oracle_mod, d):
+    H = oracle_mod.hadamard(d)
+    np.testing.assert_array_equal(H, scipy.linalg.hadamard(d) / math.sqrt(d))
+    np.testing.assert_allclose(H @ H.T, np.eye(d), atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [16, 64, 128])
+def test_rotation_preserves_inner_products(oracle_mod, d):
+    rng = np.random.default_rng(d)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    q = rng.standard_normal(d)
+    k = rng.standard_normal(d)
+    qr = oracle_mod.rotate_query(s, q)
+    kr = oracle_mod.rotate_query(s, k)
+    assert qr @ kr == pytest.approx(q @ k, rel=1e-12, abs=1e-12)
+    assert np.linalg.norm(qr) == pytest.approx(np.linalg.norm(q), rel=1e-13)
+    # the sign pattern acts before H: compare with an independent construction
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    np.testing.assert_allclose(qr, Hs @ (s * q), atol=1e-12)
+    assert not np.allclose(qr, s * (Hs @ q))
+
+
+# ----------------------------------------------------------------------------------------------
+# Write path
+# ----------------------------------------------------------------------------------------------
+
+def _independent_codes(keys, signs, levels, d):
+    """Nearest level of each rotated coordinate, via scipy's Hadamard and argmin."""
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    k = np.asarray(keys, dtype=np.float64).reshape(-1, d)
+    u = k / np.linalg.norm(k, axis=1, keepdims=True)
+    y = (u * signs) @ Hs.T
+    idx = np.argmin(np.abs(y[..., None] - np.asarray(levels)[None, None, :]), axis=-1)
+    return idx, y
+
+
+@pytest.mark.parametrize("d,b", [(16, 2), (16, 1), (32, 3), (64, 4), (128, 4), (128, 3)])
+def test_encode_codes_equal_nearest_level(oracle_mod, d, b):
+    rng = np.random.default_rng(100 + d + b)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    keys = rng.standard_normal((300, d)) * rng.lognormal(0, 1, size=(300, 1))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, y, tie = oracle_mod.encode_keys(th, s, keys, b)
+    idx, y_ind = _independent_codes(keys, s, lv, d)
+    np.testing.assert_allclose(y, y_ind, atol=1e-13)
+    np.testing.assert_allclose(norms, np.linalg.norm(keys, axis=1), rtol=1e-14)
+    got = oracle_mod.unpack_codes(codes, d, b)
+    np.testing.assert_array_equal(got, idx)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), 1.0, rtol=1e-13)
+
+
+@pytest.mark.parametrize("d,b", [(16, 2), (32, 3), (64, 4), (64, 1)])
+def test_code_packing_is_lsb_first_bitstream(oracle_mod, d, b):
+    rng = np.random.default_rng(7)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    keys = rng.standard_normal((50, d))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, _, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    idx, _ = _independent_codes(keys, s, lv, d)
+    assert codes.shape == (50, d * b // 8)
+    bits = np.unpackbits(codes, axis=1, bitorder="little").reshape(50, d, b)
+    rebuilt = (bits * (1 << np.arange(b))).sum(axis=-1)
+    np.testing.assert_array_equal(rebuilt, idx)
+
+
+def test_code_packing_hand_example(oracle_mod):
+    """d=16, b=4: a key equal to the sign-pattern-weighted first Hadamard row has y = e_0."""
+    d, b = 16, 4
+    s = np.array([1, -1] * 8, dtype=np.int8)
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    k = s * Hs[0] * 3.0  # H D k / |k| = e_0
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, y, _ = oracle_mod.encode_keys(th, s, k[None, :], b)
+    assert norms[0] == pytest.approx(3.0)
+    np.testing.assert_allclose(y[0], np.eye(d)[0], atol=1e-15)
+    # y_0 = 1 > every threshold -> code 15; every other y_i = 0 -> code 8 (the middle threshold is 0)
+    expected = np.array([0x8F] + [0x88] * 7, dtype=np.uint8)
+    np.testing.assert_array_equal(codes[0], expected)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_encode_negated_key_mirrors_codes(oracle_mod, b):
+    d = 64
+    rng = np.random.default_rng(b)
+    s = W.signs(W.LONGCTX)
+    keys = rng.standard_normal((200, d))
+    lv, th = oracle_mod.codebook(d, b)
+    cp, npos, _, tie = oracle_mod.encode_keys(th, s, keys, b)
+    cn, nneg, _, _ = oracle_mod.encode_keys(th, s, -keys, b)
+    ip = oracle_mod.unpack_codes(cp, d, b)
+    ineg = oracle_mod.unpack_codes(cn, d, b)
+    L = 1 << b
+    ok = ~tie
+    np.testing.assert_array_equal(ineg[ok], (L - 1 - ip)[ok])
+    np.testing.assert_array_equal(npos, nneg)
+
+
+def test_encode_zero_key(oracle_mod):
+    d, b = 64, 4
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, y, _ = oracle_mod.encode_keys(th, W.signs(W.LONGCTX), np.zeros((2, d)), b)
+    assert np.all(norms == 0)
+    assert np.all(oracle_mod.unpack_codes(codes, d, b) == 8)
+
+
+def test_encode_tie_band_flags(oracle_mod):
+    d, b = 16, 2
+    s = np.ones(d, dtype=np.int8)
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    lv, th = oracle_mod.codebook(d, b)
+    y = np.zeros(d)
+    y[0] = th[2] + 5e-7  # inside the band
+    y[1] = th[2] + 5e-6  # outside
+    y[2] = math.sqrt(max(0.0, 1.0 - y[0] ** 2 - y[1] ** 2))
+    k = Hs.T @ y  # H is symmetric and orthogonal, D = I
+    _, _, yo, tie = oracle_mod.encode_keys(th, s, k[None, :], b)
+    assert tie[0, 0] and not tie[0, 1]
+    assert yo[0, 0] == pytest.approx(y[0], abs=1e-15)
+
+
+# ----------------------------------------------------------------------------------------------
+# Read path
+# ----------------------------------------------------------------------------------------------
+
+def _dequant_original_domain(codes, norms, signs, levels, d, b, oracle_mod):
+    """k_hat = |k| D H^T c_hat: the inverse transform, computed independently (used only in tests)."""
+    idx = oracle_mod.unpack_codes(codes, d, b)
+    chat = np.asarray(levels)[idx]
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    return norms[..., None] * ((chat @ Hs) * signs)
+
+
+@pytest.mark.parametrize("d,b", [(16, 2), (64, 4), (128, 3)])
+def test_lut_scores_equal_bruteforce_dequant(oracle_mod, d, b):
+    rng = np.random.default_rng(11 * d + b)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    B, Hq, Hkv, T = 2, 4, 2, 37
+    q = rng.standard_normal((B, Hq, d))
+    keys = rng.standard_normal((B, Hkv, T, d)) * 2.0
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    sc = oracle_mod.scores(lv, s, q, codes, norms)
+    # route 1: rotated domain, q' . c_hat (BJ-style brute force)
+    idx = oracle_mod.unpack_codes(codes, d, b)
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    qrot = (q * s) @ Hs.T
+    G = Hq // Hkv
+    for h in range(Hq):
+        chat = np.asarray(lv)[idx[:, h // G]]  # [B, T, d]
+        ref = norms[:, h // G] * np.einsum("bd,btd->bt", qrot[:, h], chat)
+        np.testing.assert_allclose(sc[:, h], ref, rtol=1e-12, atol=1e-12)
+    # route 2: original domain, q . k_hat with the inverse transform
+    khat = _dequant_original_domain(codes, norms, s, lv, d, b, oracle_mod)
+    for h in range(Hq):
+        ref = np.einsum("bd,btd->bt", q[:, h], khat[:, h // G])
+        np.testing.assert_allclose(sc[:, h], ref, rtol=1e-11, atol=1e-11)
+
+
+def test_lut_entries(oracle_mod):
+    lv, _ = oracle_mod.codebook(16, 2)
+    qr = np.arange(16, dtype=np.float64) - 7.5
+    lut = oracle_mod.build_lut(lv, qr)
+    assert lut.shape == (16, 4)
+    np.testing.assert_array_equal(lut, np.multiply.outer(qr, lv))
+
+
+def test_b1_score_closed_form(oracle_mod):
+    d = 64
+    rng = np.random.default_rng(3)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    q = rng.standard_normal((1, 1, d))
+    keys = rng.standard_normal((1, 1, 20, d))
+    lv, th = oracle_mod.codebook(d, 1)
+    codes, norms, y, _ = oracle_mod.encode_keys(th, s, keys, 1)
+    sc = oracle_mod.scores(lv, s, q, codes, norms)
+    qr = oracle_mod.rotate_query(s, q[0, 0])
+    sgn = np.where(y[0, 0] >= 0, 1.0, -1.0)
+    ref = norms[0, 0] * math.sqrt(2 / math.pi) / math.sqrt(d) * (sgn @ qr)
+    np.testing.assert_allclose(sc[0, 0], ref, rtol=1e-12)
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_score_error_matches_quantizer_distortion(oracle_mod, b):
+    """E[(s - q.k)^2] ~= |q|^2 |k|^2 MSE_b / d: pins the codebook scale and the norm factor."""
+    d = 64
+    rng = np.random.default_rng(20 + b)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    T = 4000
+    q = rng.standard_normal((1, 1, d))
+    keys = rng.standard_normal((1, 1, T, d)) * rng.lognormal(0, 0.5, size=(1, 1, T, 1))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    sc = oracle_mod.scores(lv, s, q, codes, norms)[0, 0]
+    exact = keys[0, 0] @ q[0, 0]
+    c, t, _ = oracle_mod.lloyd_max_unit(b)
+    mse = oracle_mod.quantizer_mse_unit(b, c, t)
+    pred = np.mean(norms[0, 0] ** 2) * np.sum(q ** 2) * mse / d
+    assert np.mean((sc - exact) ** 2) == pytest.approx(pred, rel=0.25)
+
+
+def test_softmax_rows_sum_to_one(oracle_mod):
+    rng = np.random.default_rng(1)
+    for n in (1, 7, 1000):
+        p = oracle_mod.softmax_row(rng.standard_normal(n) * 30, 0.125)
+        assert p.sum() == pytest.approx(1.0, abs=1e-12)
+        assert np.all(p >= 0)
+
+
+def _torch_sdpa(q, k, v, scale, G):
+    import torch
+    qt = torch.from_numpy(np.asarray(q, dtype=np.float64))[:, :, None, :]  # [B, Hq, 1, d]
+    kt = torch.from_numpy(np.asarray(k, dtype=np.float64)).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(np.asarray(v, dtype=np.float64)).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o[:, :, 0, :].numpy()
+
+
+@pytest.mark.parametrize("d,b,G", [(16, 2, 1), (64, 4, 8), (128, 3, 4)])
+def test_decode_attn_equals_sdpa_on_dequantized_keys(oracle_mod, d, b, G):
+    rng = np.random.default_rng(d * b + G)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    B, Hkv, T = 2, 2, 50
+    Hq = Hkv * G
+    q = rng.standard_normal((B, Hq, d)) * 3
+    keys = rng.standard_normal((B, Hkv, T, d)) * 2
+    v = rng.standard_normal((B, Hkv, T, d))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    scale = 1.0 / math.sqrt(d)
+    out = oracle_mod.decode_attn(lv, s, q, codes, norms, v, scale)
+    khat = _dequant_original_domain(codes, norms, s, lv, d, b, oracle_mod)
+    ref = _torch_sdpa(q, khat, v, scale, G)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_decode_attn_special_cases(oracle_mod):
+    d, b = 64, 4
+    rng = np.random.default_rng(9)
+    s = W.signs(W.LONGCTX)
+    B, Hkv, T = 1, 1, 40
+    keys = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    # zero query: uniform attention -> mean of V
+    out = oracle_mod.decode_attn(lv, s, np.zeros((1, 1, d)), codes, norms, v, 0.125)
+    np.testing.assert_allclose(out[0, 0], v[0, 0].mean(axis=0), atol=1e-14)
+    # one key with a huge norm aligned with q dominates -> output = its value row
+    norms2 = norms.copy()
+    norms2[0, 0, 17] = 1e6
+    q = oracle_mod_rotate_back(oracle_mod, s, lv, codes[0, 0, 17], d, b)
+    out = oracle_mod.decode_attn(lv, s, q[None, None, :], codes, norms2, v, 1.0)
+    np.testing.assert_allclose(out[0, 0], v[0, 0, 17], atol=1e-12)
+
+
+def oracle_mod_rotate_back(oracle_mod, s, lv, code_row, d, b):
+    """A query whose score against this code row is maximal: D H^T c_hat."""
+    idx = oracle_mod.unpack_codes(code_row[None, :], d, b)[0]
+    Hs = scipy.linalg.hadamard(d) / math.sqrt(d)
+    return (np.asarray(lv)[idx] @ Hs) * s
+
+
+def test_seq_lens_truncate_and_empty(oracle_mod):
+    d, b = 16, 2
+    rng = np.random.default_rng(4)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    B, Hq, Hkv, T = 3, 2, 1, 30
+    q = rng.standard_normal((B, Hq, d))
+    keys = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    lens = np.array([30, 0, 11], dtype=np.int32)
+    out = oracle_mod.decode_attn(lv, s, q, codes, norms, v, 0.25, seq_lens=lens)
+    assert np.all(out[1] == 0)
+    sub = oracle_mod.decode_attn(lv, s, q[2:3], codes[2:3, :, :11], norms[2:3, :, :11], v[2:3, :, :11], 0.25)
+    np.testing.assert_allclose(out[2], sub[0], rtol=1e-14)
+    full = oracle_mod.decode_attn(lv, s, q, codes, norms, v, 0.25)
+    np.testing.assert_array_equal(out[0], full[0])
+    sc = oracle_mod.scores(lv, s, q, codes, norms, seq_lens=lens)
+    assert np.all(np.isneginf(sc[1])) and np.all(np.isneginf(sc[2, :, 11:])) and np.all(np.isfinite(sc[2, :, :11]))
+
+
+# ----------------------------------------------------------------------------------------------
+# Product quantization
+# ----------------------------------------------------------------------------------------------
+
+def test_kmeans_objective_never_increases(oracle_mod):
+    rng = np.random.default_rng(0)
+    train = rng.standard_normal((2000, 8))
+    init = rng.permutation(2000)[:64]
+    cent, obj = oracle_mod.kmeans(train, 64, 10, init)
+    assert np.all(np.diff(obj) <= 1e-12)
+    assert obj[-1] < obj[0]
+
+
+def test_kmeans_all_points_as_centroids_is_exact(oracle_mod):
+    rng = np.random.default_rng(1)
+    train = rng.standard_normal((50, 4))
+    cent, obj = oracle_mod.kmeans(train, 50, 3, np.arange(50))
+    assert obj[-1] == 0.0
+    np.testing.assert_array_equal(cent, train)
+
+
+def test_kmeans_matches_sklearn_lloyd(oracle_mod):
+    from sklearn.cluster import KMeans
+    rng = np.random.default_rng(2)
+    train = rng.standard_normal((3000, 8))
+    init_rows = rng.permutation(3000)[:32]
+    iters = 10
+    cent, _ = oracle_mod.kmeans(train, 32, iters, init_rows)
+    km = KMeans(n_clusters=32, init=train[init_rows], n_init=1, max_iter=iters, tol=0.0,
+                algorithm="lloyd").fit(train)
+    # sklearn ends with the centroid update of its last iteration; so does the oracle
+    np.testing.assert_allclose(cent, km.cluster_centers_, rtol=1e-9, atol=1e-9)
+
+
+def test_kmeans_scalar_subspaces(oracle_mod):
+    """m = d: one-dimensional k-means; the nearest-centroid cells are intervals between midpoints."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4000, 1))
+    cent, _ = oracle_mod.kmeans(x, 8, 50, rng.permutation(4000)[:8])
+    cs = np.sort(cent[:, 0])
+    # at a converged 1-D k-means, each centroid is the mean of the points between its midpoints
+    edges = np.concatenate([[-np.inf], 0.5 * (cs[1:] + cs[:-1]), [np.inf]])
+    for j in range(8):
+        sel = (x[:, 0] >= edges[j]) & (x[:, 0] < edges[j + 1])
+        assert x[sel, 0].mean() == pytest.approx(cs[j], abs=2e-3)
+
+
+def test_pq_encode_nearest_centroid(oracle_mod):
+    rng = np.random.default_rng(8)
+    d, m, K = 64, 8, 256
+    cent = rng.standard_normal((m, K, d // m))
+    keys = rng.standard_normal((100, d))
+    codes, gap = oracle_mod.pq_encode(cent, keys)
+    for s in range(m):
+        sub = keys[:, s * 8:(s + 1) * 8]
+        dist = ((sub[:, None, :] - cent[s][None, :, :]) ** 2).sum(-1)
+        np.testing.assert_array_equal(codes[:, s], np.argmin(dist, axis=1))
+        sd = np.sort(dist, axis=1)
+        np.testing.assert_allclose(gap[:, s], sd[:, 1] - sd[:, 0], rtol=1e-9, atol=1e-12)
+
+
+def test_pq_scores_and_attention_equal_dequantized(oracle_mod):
+    rng = np.random.default_rng(10)
+    d, m, K = 64, 8, 16
+    B, H, T = 2, 3, 40
+    cent = rng.standard_normal((H, m, K, d // m))
+    q = rng.standard_normal((B, H, d))
+    keys = rng.standard_normal((B, H, T, d))
+    v = rng.standard_normal((B, H, T, d))
+    codes = np.zeros((B, H, T, m), dtype=np.uint8)
+    for h in range(H):
+        codes[:, h] = oracle_mod.pq_encode(cent[h], keys[:, h])[0]
+    sc = oracle_mod.pq_scores(cent, q, codes)
+    khat = np.zeros((B, H, T, d))
+    for h in range(H):
+        for s in range(m):
+            khat[:, h, :, s * 8:(s + 1) * 8] = cent[h, s][codes[:, h, :, s]]
+    np.testing.assert_allclose(sc, np.einsum("bhd,bhtd->bht", q, khat), rtol=1e-12, atol=1e-12)
+    out = oracle_mod.pq_decode_attn(cent, q, codes, v, 0.125)
+    np.testing.assert_allclose(out, _torch_sdpa(q, khat, v, 0.125, 1), rtol=1e-10, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------------------------
+# Workload generators: seeded and reproducible per batch slice
+# ----------------------------------------------------------------------------------------------
+
+def test_workloads_are_deterministic_and_sliceable():
+    sh = W.scaled(W.LONGCTX, B=3, T=100)
+    a = W.keys(sh)
+    b = W.keys(sh, batches=[2])
+    np.testing.assert_array_equal(a[2], b[0])
+    np.testing.assert_array_equal(W.values(sh), W.values(sh))
+    s = W.signs(sh)
+    assert set(np.unique(s)) <= {-1, 1}
+    assert a.dtype == np.float16
