@@ -1,0 +1,195 @@
+"""Benchmark: fused LUT decode attention from 4-bit Hadamard/Lloyd-Max key codes.
+
+One step = one decode step of the whole hot path on one GPU:
+  1. write path: encode the new token's key of every (batch, kv head) into the
+     code cache (norm + packed codes) at position T-1;
+  2. read path: rotate the queries, build the per-head LUTs in LDS, score all
+     T cached keys from their codes, online softmax, AV product over fp16 V,
+     split merge -> attention output [B][Hq][d].
+
+Workload (default): B=8, Hq=32, Hkv=4, d=64, b=4, T=32768 (1.1B-Llama-like
+long-context decode), seeded synthetic inputs.  R >= 4 copies of the cache at
+distinct addresses are rotated so every step streams from HBM rather than the
+256 MB last-level cache.
+
+Prints ONE JSON line on stdout (human-readable detail on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "keys scored/sec and % of HBM roofline, fused 4-bit LUT decode attn, B=8 T=32k"
+HBM_PEAK_GBS = 8000.0
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shape, bpk):
+    """Bytes the read path must move per call: codes + fp32 norms + V + q (outputs not credited)."""
+    keys = shape.B * shape.Hkv * shape.T
+    vb = 2 if shape.dtype == "f16" else 4
+    return keys * (bpk + 4 + shape.d * vb) + shape.B * shape.Hq * shape.d * vb
+
+
+def cpu_baseline(shape, signs, q, min_seconds=5.0):
+    """Time the fp64 oracle (one thread) on the same decode step: all batches, repeated until min_seconds pass."""
+    import oracle
+    import workloads as W
+
+    lv, th = oracle.codebook(shape.d, shape.b)
+    scale = 1.0 / math.sqrt(shape.d)
+    cache = []
+    for bi in range(shape.B):  # the prefilled cache: encoded by the oracle itself, untimed
+        keys = W.keys(shape, batches=[bi])
+        codes, norms, _, _ = oracle.encode_keys(th, signs, keys, shape.b)
+        cache.append((codes, norms, W.values(shape, batches=[bi])))
+    newk = W.new_keys(shape)
+    done_keys, elapsed, passes = 0, 0.0, 0
+    while elapsed < min_seconds or passes == 0:
+        t0 = time.perf_counter()
+        oracle.encode_keys(th, signs, newk, shape.b)                              # write path of the step
+        for bi, (codes, norms, v) in enumerate(cache):
+            oracle.decode_attn(lv, signs, q[bi:bi + 1], codes, norms, v, scale)  # read path of the step
+        elapsed += time.perf_counter() - t0
+        done_keys += shape.B * shape.Hq * shape.T
+        passes += 1
+    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": "the full decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode of the new "
+                      "keys + decode attention, one thread, %.1f s" % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--caches", type=int, default=4, help="distinct cache copies rotated across steps")
+    ap.add_argument("--splits", type=int, default=0, help="T splits (0 = library's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % a.gpus)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from quantized_kv_cache_encode_amd import build as kbuild
+
+    if kbuild.is_stale():
+        eprint("libkvq.so missing or stale: building")
+        kbuild.build()
+    import quantized_kv_cache_encode_amd.kvq as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    shape = W.LONGCTX
+    B, Hq, Hkv, d, T, b = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T, shape.b
+
+    eprint("generating %s: B=%d Hq=%d Hkv=%d d=%d b=%d T=%d" % (shape.name, B, Hq, Hkv, d, b, T))
+    signs = W.signs(shape)
+    q_np = W.queries(shape)
+    keys = torch.from_numpy(W.keys(shape)).to(dev)
+    v0 = torch.from_numpy(W.values(shape)).to(dev)
+    newk = torch.from_numpy(W.new_keys(shape)).to(dev)
+    q = torch.from_numpy(q_np).to(dev)
+    cb = K.kvq_build_codebook(d, b)
+    bpk = cb.bytes_per_key
+
+    # prefill: encode the whole cache once (setup), then make R copies at distinct addresses
+    codes0 = torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev)
+    norms0 = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+    K.kvq_encode_keys(cb, signs, keys, codes0, norms0)
+    del keys
+    caches = [(codes0, norms0, v0)] + [(codes0.clone(), norms0.clone(), v0.clone()) for _ in range(a.caches - 1)]
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+    ws_bytes = K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, a.splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c, n, v = caches[i % len(caches)]
+        K.kvq_encode_keys(cb, signs, newk, c, n, t0=T - 1)
+        if ev is not None:
+            ev[0].record()
+        K.kvq_decode_attn(cb, signs, q, c, n, v, out=out, workspace=ws, n_splits=a.splits)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps between two synchronizations
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(a.steps):
+        step(i, kev[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_per_step = total_ms / a.steps
+    attn_ms = [e0.elapsed_time(e1) for e0, e1 in kev]
+    attn_avg_ms = sum(attn_ms) / len(attn_ms)
+
+    key_scores = B * Hq * T
+    value = key_scores / (ms_per_step * 1e-3)
+    alg_bytes = algorithmic_bytes(shape, bpk)
+    achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
+    splits_used = ws_bytes // (B * Hq * (d + 2) * 4) if ws_bytes else 1
+    eprint("step %.4f ms  (decode attention %.4f ms avg, min %.4f)  -> %.4g key-scores/s" %
+           (ms_per_step, attn_avg_ms, min(attn_ms), value))
+    eprint("decode attention: %d algorithmic bytes -> %.1f GB/s = %.1f%% of %.0f GB/s" %
+           (alg_bytes, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        eprint("timing the CPU oracle on a bounded sample (~%.0f s)" % a.cpu_seconds)
+        cpu = cpu_baseline(shape, signs, q_np, a.cpu_seconds)
+        eprint("cpu oracle: %.4g key-scores/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "longctx decode: B=8 Hq=32 Hkv=4 d=64 b=4 T=32768, fp16 q/k/v",
+                   "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "b": b, "T": T, "v_dtype": "f16",
+                   "step": "encode B*Hkv new keys + fused decode attention over T keys",
+                   "caches_rotated": len(caches), "t_splits": int(splits_used)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kvq decode attention (decode_kernel + split combine)",
+                     "avg_launch_ms": attn_avg_ms, "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

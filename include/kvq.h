@@ -1,0 +1,184 @@
+/*
+ * kvq.h -- C ABI of libkvq: attention computed directly from quantized
+ * key-cache codes on AMD Instinct MI355X (gfx950).
+ *
+ * Method (web pages, cited by title and section):
+ *   "AXELRAM: Quantize Once, Never Dequantize" -- Key Points and Abstract:
+ *     keys are transformed on write (an orthogonal transform with a +-1 sign
+ *     pattern, which spreads every coordinate of the rotated unit key like
+ *     N(0, 1/d)) and stored as indices of a codebook fixed at design time that
+ *     depends only on the head dimension d and the bit width b; on read the
+ *     query is transformed once and scores come from table lookups over the
+ *     stored indices, with no inverse transform.
+ *   "LOOKAT: Lookup-Optimized Key-Attention" summary page -- AI Summary and
+ *     Abstract: product quantization (m subspaces, a learned codebook each)
+ *     with asymmetric distance computation through lookup tables.
+ *   Shift-accumulate attention page (arxivdaily 2609.09208) -- English
+ *     abstract: a fused decode-attention kernel with online softmax.
+ *
+ * Concretely, with H the normalised Sylvester Walsh-Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i&j) / sqrt(d)) and D = diag(signs):
+ *   write:  n = ||k||,  y = H D k / n,  code_i = #{ j : t_j <= y_i }
+ *           (t = thresholds of the Lloyd-Max codebook for N(0, 1/d))
+ *   read:   q' = H D q,  LUT[i][j] = q'_i * c_j,
+ *           s_t = n_t * sum_i LUT[i][code_{t,i}],
+ *           out = sum_t softmax_t(scale * s) * v_t
+ *   PQ:     LUT[s][c] = q_s . C_{s,c},  s_t = sum_s LUT[s][code_{t,s}]
+ *
+ * Conventions shared by every entry point
+ *   - Layouts are row-major and contiguous.  B = batch, Hq = query heads,
+ *     Hkv = key/value heads (Hq % Hkv == 0; query head h reads kv head
+ *     h / (Hq/Hkv)), T_cap = capacity of the cache along the token axis,
+ *     d = head dimension.
+ *   - Codes are packed LSB-first: coordinate i of a key occupies bits
+ *     [i*b, i*b + b) of the key's byte row of d*b/8 bytes, bit 0 of byte 0
+ *     first (for b = 4: low nibble = even coordinate).
+ *   - Every pointer marked "device" is caller-owned device memory (e.g. a
+ *     PyTorch tensor); the library never allocates, frees or retains it.
+ *     Pointers marked "host" are read during the call only.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t; NULL
+ *     means the default stream); outputs are valid once the caller
+ *     synchronizes that stream.  Calls are reentrant; two calls that write
+ *     the same buffers must be ordered by the caller.
+ *   - Every function validates its arguments before launching anything and
+ *     returns a kvq_status; on failure nothing is launched and
+ *     kvq_last_error() describes the problem.  The library never prints,
+ *     aborts or throws across this boundary.
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1, /* a size, pointer, alignment or enum is out of range */
+  KVQ_ERR_UNSUPPORTED = 2, /* valid but not built (e.g. an untemplated d) */
+  KVQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  KVQ_ERR_DEVICE = 4       /* a HIP call failed; the HIP error string is in kvq_last_error() */
+} kvq_status;
+
+typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_F16 = 1 } kvq_dtype;
+
+typedef enum kvq_kind {
+  KVQ_HADAMARD_LM = 0, /* Walsh-Hadamard rotation + Lloyd-Max scalar codebook */
+  KVQ_PQ = 1           /* product quantization, asymmetric distance computation */
+} kvq_kind;
+
+#define KVQ_MAX_LEVELS 16
+
+/* A codebook.  Plain data: copy it freely.  For KVQ_HADAMARD_LM it is fully
+ * described by (d, b) and the arrays; for KVQ_PQ it refers to caller-owned
+ * device centroids. */
+typedef struct kvq_codebook {
+  int32_t kind;                            /* kvq_kind */
+  int32_t d;                               /* head dimension */
+  int32_t b;                               /* HLM: bits per coordinate, 1..4 */
+  int32_t m;                               /* PQ: number of subspaces (d % m == 0) */
+  int32_t K;                               /* PQ: centroids per subspace, 2..256 */
+  int32_t n_heads;                         /* PQ: kv heads covered by pq_centroids */
+  float levels[KVQ_MAX_LEVELS];            /* HLM: ascending levels c_0..c_{2^b-1} */
+  float thresholds[KVQ_MAX_LEVELS - 1];    /* HLM: t_j = (c_j + c_{j+1}) / 2 */
+  const float* pq_centroids;               /* PQ: device [n_heads][m][K][d/m] fp32 */
+} kvq_codebook;
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kvq_version(void);
+
+/* Thread-local, NUL-terminated description of the last failure on this
+ * thread ("" if none).  Valid until the next kvq_* call on the thread. */
+const char* kvq_last_error(void);
+
+/* Lloyd-Max codebook for N(0, 1/d) with 2^b levels (AXELRAM, Abstract: the
+ * quantizer depends only on d and b).  Host only, deterministic: the Lloyd
+ * iteration on N(0,1) in double precision, made exactly odd-symmetric, scaled
+ * by 1/sqrt(d) and rounded to fp32; thresholds are the midpoints.
+ *   d: power of two, 16 <= d <= 256.   b: 1..4.   out: host, written.
+ * Errors: KVQ_ERR_INVALID_ARG for d, b out of range or out == NULL. */
+kvq_status kvq_build_codebook(int d, int b, kvq_codebook* out);
+
+/* Product-quantization codebooks by Lloyd k-means (LOOKAT, AI Summary:
+ * codebook learning per subspace).  Host only, double precision.
+ *   train:      host [H][n][d] fp32 training keys.
+ *   start_rows: host [H][m][K] int64, rows of train[h] that seed the
+ *               centroids of (h, s) (sub-vector s of those rows); each in [0, n).
+ *   iters:      assignment/update rounds (>= 0).  Ties go to the lowest
+ *               centroid index; a centroid with no members keeps its place.
+ *   centroids:  host [H][m][K][d/m] fp32, written.
+ * Errors: KVQ_ERR_INVALID_ARG for sizes out of range (d % m != 0, K > 256,
+ *   K > n, a start row out of range) or NULL pointers. */
+kvq_status kvq_build_codebook_pq(const float* train, int H, int64_t n, int d, int m, int K, int iters,
+                                 const int64_t* start_rows, float* centroids);
+
+/* Fill a KVQ_PQ codebook that refers to device centroids
+ * [n_heads][m][K][d/m] fp32 (caller-owned; must outlive every call using
+ * the codebook).  Host only. */
+kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centroids_device, kvq_codebook* out);
+
+/* Write path: encode keys into the code cache (AXELRAM, Abstract: transform on
+ * write).
+ *   cb:        codebook (HLM or PQ).
+ *   signs:     host [d] int8, each +1 or -1 (HLM); ignored for PQ (may be NULL).
+ *   keys:      device [B][Hkv][T_new][d], dtype kdtype (may be NULL when T_new == 0).
+ *   codes:     device [B][Hkv][T_cap][d*b/8] (HLM) or [B][Hkv][T_cap][m] (PQ)
+ *              uint8; rows pos_b .. pos_b+T_new-1 of every (b, h) are written.
+ *   norms:     device [B][Hkv][T_cap] fp32, same rows written (HLM);
+ *              ignored for PQ (may be NULL).
+ *   t0:        write position used for every batch when write_pos is NULL.
+ *   write_pos: device [B] int32 per-batch write positions, or NULL.
+ *              Rows that would fall outside [0, T_cap) are skipped.
+ *   For PQ the kv head index selects that head's centroids (Hkv == n_heads).
+ * A zero key gets norm 0 and the codes of the zero vector; NaN propagates to
+ * the norm (its codes are then unspecified).
+ * Errors: KVQ_ERR_INVALID_ARG (sizes, NULL, misaligned, signs not +-1, t0 out
+ *   of range when write_pos == NULL), KVQ_ERR_UNSUPPORTED (d, b not built),
+ *   KVQ_ERR_DEVICE. */
+kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const void* keys, kvq_dtype kdtype,
+                           int B, int Hkv, int64_t T_new, uint8_t* codes, float* norms, int64_t T_cap,
+                           int64_t t0, const int32_t* write_pos, void* stream);
+
+/* Read path, scores only (AXELRAM, Abstract: table lookup on read; LOOKAT for
+ * PQ).  scores[b][h][t] = raw estimate of q.k_t (no softmax scale) for
+ * t < len_b; scores at t >= len_b are set to -inf.
+ *   q:        device [B][Hq][d], dtype qdtype.
+ *   codes, norms: as written by kvq_encode_keys (norms ignored for PQ).
+ *   seq_lens: device [B] int32 valid lengths (0..T_cap), or NULL for T_cap.
+ *   scores:   device [B][Hq][T_cap] fp32, written.
+ * Errors: as kvq_encode_keys. */
+kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                     const uint8_t* codes, const float* norms, int B, int Hq, int Hkv, int64_t T_cap,
+                     const int32_t* seq_lens, float* scores, void* stream);
+
+/* Bytes of device workspace kvq_decode_attn needs for this shape and split
+ * count (n_splits = 0: the library's choice).  0 on invalid arguments. */
+size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv, int64_t T_cap, int n_splits);
+
+/* Fused decode attention from codes: scores, online softmax over t of
+ * scale * s, and the AV product over v, in one pass over the cache split
+ * along T across workgroups, followed by a log-sum-exp merge of the splits.
+ *   v:        device [B][Hkv][T_cap][d], dtype vdtype.
+ *   scale:    softmax scale (1/sqrt(d) for standard attention).
+ *   out:      device [B][Hq][d], dtype odtype, written.  A sequence of
+ *             length 0 gives zeros.
+ *   workspace: device, at least kvq_decode_attn_workspace(...) bytes with the
+ *             same n_splits; contents on entry are ignored.
+ *   n_splits: 0 = library's choice; otherwise 1..T_cap/64 rounded up (the
+ *             result is the same up to rounding for every n_splits).
+ * Errors: as kvq_encode_keys, plus KVQ_ERR_WORKSPACE. */
+kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                           const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
+                           int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
+                           void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,19 @@
+"""Attention computed directly from quantized key-cache codes on AMD MI355X.
+
+The computation runs in libkvq.so (hand-written HIP for gfx950, C ABI in
+include/kvq.h); ``quantized_kv_cache_encode_amd.kvq`` is its Python binding.
+Importing the binding fails if the library has not been built
+(``python -m quantized_kv_cache_encode_amd.build``).
+"""
+import importlib
+
+__all__ = ["kvq"]
+
+
+def __getattr__(name):
+    if name == "kvq":
+        return importlib.import_module(".kvq", __name__)
+    mod = importlib.import_module(".kvq", __name__)
+    if hasattr(mod, name):
+        return getattr(mod, name)
+    raise AttributeError(name)

@@ -1,0 +1,319 @@
+// Host side of the libkvq C ABI (include/kvq.h): argument validation, codebook
+// construction, launch geometry and kernel dispatch.  No device memory is
+// allocated here; every buffer belongs to the caller.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "%s: this shape/dtype combination is not built", what);
+  return fail(KVQ_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+kvq_status check_codebook(const kvq_codebook* cb) {
+  if (!cb) return fail(KVQ_ERR_INVALID_ARG, "codebook is NULL");
+  if (cb->kind == KVQ_HADAMARD_LM) {
+    if (!pow2(cb->d) || cb->d < 16 || cb->d > 256)
+      return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", cb->d);
+    if (cb->b < 1 || cb->b > 4) return fail(KVQ_ERR_INVALID_ARG, "b=%d: must be 1..4", cb->b);
+    return KVQ_OK;
+  }
+  if (cb->kind == KVQ_PQ) {
+    if (cb->d <= 0 || cb->m <= 0 || cb->d % cb->m != 0)
+      return fail(KVQ_ERR_INVALID_ARG, "PQ d=%d, m=%d: m must divide d", cb->d, cb->m);
+    if (cb->K < 2 || cb->K > 256) return fail(KVQ_ERR_INVALID_ARG, "PQ K=%d: must be 2..256", cb->K);
+    if (!cb->pq_centroids) return fail(KVQ_ERR_INVALID_ARG, "PQ centroids pointer is NULL");
+    if (!aligned16(cb->pq_centroids)) return fail(KVQ_ERR_INVALID_ARG, "PQ centroids not 16-byte aligned");
+    if (cb->n_heads <= 0) return fail(KVQ_ERR_INVALID_ARG, "PQ n_heads=%d", cb->n_heads);
+    return KVQ_OK;
+  }
+  return fail(KVQ_ERR_INVALID_ARG, "unknown codebook kind %d", cb->kind);
+}
+
+int bytes_per_key(const kvq_codebook* cb) { return cb->kind == KVQ_PQ ? cb->m : cb->d * cb->b / 8; }
+
+kvq_status pack_signs(const int8_t* signs, int d, uint32_t out[8]) {
+  for (int k = 0; k < 8; ++k) out[k] = 0;
+  if (!signs) return fail(KVQ_ERR_INVALID_ARG, "signs is NULL");
+  for (int i = 0; i < d; ++i) {
+    if (signs[i] == -1) out[i >> 5] |= 1u << (i & 31);
+    else if (signs[i] != 1) return fail(KVQ_ERR_INVALID_ARG, "signs[%d]=%d: must be +1 or -1", i, (int)signs[i]);
+  }
+  return KVQ_OK;
+}
+
+bool valid_dtype(int t) { return t == KVQ_F32 || t == KVQ_F16; }
+
+// Largest power of two <= 8 dividing G: query heads served by one workgroup.
+int heads_per_wg(int G) {
+  for (int gg = 8; gg > 1; gg >>= 1)
+    if (G % gg == 0) return gg;
+  return 1;
+}
+
+// Split of the token axis: every split is a multiple of 64 tokens.  With no
+// request, aim for about 1024 workgroups (four per compute unit) but keep at
+// least 256 tokens (one chunk per wave) in a split.
+void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len) {
+  const int64_t max_splits = (T_cap + 63) / 64;
+  int64_t s;
+  if (requested > 0) {
+    s = requested < max_splits ? requested : max_splits;
+  } else {
+    s = (1024 + units - 1) / units;
+    const int64_t cap = (T_cap + 255) / 256;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+  }
+  int64_t len = (T_cap + s - 1) / s;
+  len = (len + 63) / 64 * 64;
+  *split_len = len;
+  *n_splits = (int)((T_cap + len - 1) / len);
+}
+
+struct ReadShape {
+  int gg, n_groups;
+  int64_t units;
+};
+
+kvq_status check_read(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                      const uint8_t* codes, const float* norms, int B, int Hq, int Hkv, int64_t T_cap,
+                      kvq::AttnParams* p, ReadShape* rs) {
+  kvq_status st = check_codebook(cb);
+  if (st != KVQ_OK) return st;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0) return fail(KVQ_ERR_INVALID_ARG, "B=%d Hq=%d Hkv=%d must be positive", B, Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(KVQ_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (T_cap <= 0) return fail(KVQ_ERR_INVALID_ARG, "T_cap=%lld must be positive", (long long)T_cap);
+  if ((int64_t)B * Hkv > 65535 * 8) return fail(KVQ_ERR_INVALID_ARG, "B*Hkv too large");
+  if (!valid_dtype(qdtype)) return fail(KVQ_ERR_INVALID_ARG, "bad q dtype %d", (int)qdtype);
+  if (!q || !codes) return fail(KVQ_ERR_INVALID_ARG, "q or codes is NULL");
+  if (!aligned16(q) || !aligned16(codes)) return fail(KVQ_ERR_INVALID_ARG, "q or codes not 16-byte aligned");
+  std::memset(p, 0, sizeof *p);
+  if (cb->kind == KVQ_HADAMARD_LM) {
+    if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms is NULL");
+    if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
+    st = pack_signs(signs, cb->d, p->signs);
+    if (st != KVQ_OK) return st;
+    for (int j = 0; j < 16; ++j) p->levels[j] = j < (1 << cb->b) ? cb->levels[j] : 0.0f;
+  } else {
+    if (cb->n_heads != Hkv) return fail(KVQ_ERR_INVALID_ARG, "PQ codebook has %d heads, Hkv=%d", cb->n_heads, Hkv);
+    p->pq_cent = cb->pq_centroids;
+    p->pq_K = cb->K;
+  }
+  const int G = Hq / Hkv;
+  rs->gg = heads_per_wg(G);
+  rs->n_groups = G / rs->gg;
+  rs->units = (int64_t)B * Hkv * rs->n_groups;
+  if (rs->units > 65535) return fail(KVQ_ERR_INVALID_ARG, "B*Hkv*(head groups)=%lld exceeds the grid", (long long)rs->units);
+  p->q = q;
+  p->q_f16 = qdtype == KVQ_F16;
+  p->codes = codes;
+  p->norms = norms;
+  p->T_cap = T_cap;
+  p->B = B;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->G = G;
+  p->n_groups = rs->n_groups;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_version(void) { return 100; }
+
+const char* kvq_last_error(void) { return g_last_error.c_str(); }
+
+kvq_status kvq_build_codebook(int d, int b, kvq_codebook* out) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+  if (!pow2(d) || d < 16 || d > 256) return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", d);
+  if (b < 1 || b > 4) return fail(KVQ_ERR_INVALID_ARG, "b=%d: must be 1..4", b);
+  std::memset(out, 0, sizeof *out);
+  double lv[16], th[15];
+  kvq::lloyd_max_gaussian(b, lv, th);
+  const double s = 1.0 / std::sqrt((double)d);
+  const int L = 1 << b;
+  for (int j = 0; j < L; ++j) out->levels[j] = (float)(lv[j] * s);
+  for (int j = 0; j + 1 < L; ++j) out->thresholds[j] = (float)(th[j] * s);
+  out->kind = KVQ_HADAMARD_LM;
+  out->d = d;
+  out->b = b;
+  return ok();
+}
+
+kvq_status kvq_build_codebook_pq(const float* train, int H, int64_t n, int d, int m, int K, int iters,
+                                 const int64_t* start_rows, float* centroids) {
+  if (!train || !start_rows || !centroids) return fail(KVQ_ERR_INVALID_ARG, "NULL pointer");
+  if (H <= 0 || n <= 0 || d <= 0 || m <= 0 || d % m != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "H=%d n=%lld d=%d m=%d: need positive sizes and m | d", H, (long long)n, d, m);
+  if (K < 2 || K > 256 || K > n) return fail(KVQ_ERR_INVALID_ARG, "K=%d: must be 2..256 and <= n", K);
+  if (iters < 0) return fail(KVQ_ERR_INVALID_ARG, "iters=%d", iters);
+  for (int64_t x = 0; x < (int64_t)H * m * K; ++x)
+    if (start_rows[x] < 0 || start_rows[x] >= n)
+      return fail(KVQ_ERR_INVALID_ARG, "start_rows[%lld]=%lld out of range", (long long)x, (long long)start_rows[x]);
+  const int ds = d / m;
+  std::vector<double> cent((size_t)K * ds);
+  for (int h = 0; h < H; ++h)
+    for (int s = 0; s < m; ++s) {
+      kvq::kmeans_lloyd(train + (size_t)h * n * d + (size_t)s * ds, n, ds, d, K, iters,
+                        start_rows + ((size_t)h * m + s) * K, cent.data());
+      float* dst = centroids + ((size_t)h * m + s) * K * ds;
+      for (size_t x = 0; x < cent.size(); ++x) dst[x] = (float)cent[x];
+    }
+  return ok();
+}
+
+kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centroids_device, kvq_codebook* out) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+  std::memset(out, 0, sizeof *out);
+  out->kind = KVQ_PQ;
+  out->d = d;
+  out->m = m;
+  out->K = K;
+  out->n_heads = n_heads;
+  out->pq_centroids = centroids_device;
+  kvq_status st = check_codebook(out);
+  return st == KVQ_OK ? ok() : st;
+}
+
+kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const void* keys, kvq_dtype kdtype,
+                           int B, int Hkv, int64_t T_new, uint8_t* codes, float* norms, int64_t T_cap, int64_t t0,
+                           const int32_t* write_pos, void* stream) {
+  kvq_status st = check_codebook(cb);
+  if (st != KVQ_OK) return st;
+  if (B <= 0 || Hkv <= 0 || T_new < 0 || T_cap <= 0)
+    return fail(KVQ_ERR_INVALID_ARG, "B=%d Hkv=%d T_new=%lld T_cap=%lld out of range", B, Hkv, (long long)T_new,
+                (long long)T_cap);
+  if (!valid_dtype(kdtype)) return fail(KVQ_ERR_INVALID_ARG, "bad key dtype %d", (int)kdtype);
+  if ((!keys && T_new > 0) || !codes) return fail(KVQ_ERR_INVALID_ARG, "keys or codes is NULL");
+  if (!aligned16(keys) || !aligned16(codes)) return fail(KVQ_ERR_INVALID_ARG, "keys or codes not 16-byte aligned");
+  if (!write_pos && (t0 < 0 || t0 + T_new > T_cap))
+    return fail(KVQ_ERR_INVALID_ARG, "rows [%lld, %lld) do not fit T_cap=%lld", (long long)t0, (long long)(t0 + T_new),
+                (long long)T_cap);
+  if ((int64_t)B * Hkv > 65535) return fail(KVQ_ERR_INVALID_ARG, "B*Hkv too large");
+  kvq::EncodeParams p;
+  std::memset(&p, 0, sizeof p);
+  p.keys = keys;
+  p.codes = codes;
+  p.norms = norms;
+  p.write_pos = write_pos;
+  p.T_new = T_new;
+  p.T_cap = T_cap;
+  p.t0 = t0;
+  p.B = B;
+  p.Hkv = Hkv;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (cb->kind == KVQ_HADAMARD_LM) {
+    if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms is NULL");
+    if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
+    st = pack_signs(signs, cb->d, p.signs);
+    if (st != KVQ_OK) return st;
+    for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
+    if (T_new == 0) return ok();
+    return from_hip(kvq::launch_hlm_encode(cb->d, cb->b, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
+  }
+  if (cb->n_heads != Hkv) return fail(KVQ_ERR_INVALID_ARG, "PQ codebook has %d heads, Hkv=%d", cb->n_heads, Hkv);
+  p.pq_cent = cb->pq_centroids;
+  p.pq_K = cb->K;
+  if (T_new == 0) return ok();
+  return from_hip(kvq::launch_pq_encode(cb->d, cb->m, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
+}
+
+kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                     const uint8_t* codes, const float* norms, int B, int Hq, int Hkv, int64_t T_cap,
+                     const int32_t* seq_lens, float* scores, void* stream) {
+  kvq::AttnParams p;
+  ReadShape rs;
+  kvq_status st = check_read(cb, signs, q, qdtype, codes, norms, B, Hq, Hkv, T_cap, &p, &rs);
+  if (st != KVQ_OK) return st;
+  if (!scores || !aligned16(scores)) return fail(KVQ_ERR_INVALID_ARG, "scores NULL or not 16-byte aligned");
+  p.seq_lens = seq_lens;
+  p.scores = scores;
+  choose_splits(rs.units, T_cap, 0, &p.n_splits, &p.split_len);
+  const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (cb->kind == KVQ_HADAMARD_LM) return from_hip(kvq::launch_hlm_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");
+  return from_hip(kvq::launch_pq_score(cb->d, cb->m, rs.gg, p, grid, s), "kvq_score");
+}
+
+size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv, int64_t T_cap, int n_splits) {
+  if (check_codebook(cb) != KVQ_OK || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || T_cap <= 0 || n_splits < 0)
+    return 0;
+  const int G = Hq / Hkv;
+  const int gg = heads_per_wg(G);
+  int splits;
+  int64_t len;
+  choose_splits((int64_t)B * Hkv * (G / gg), T_cap, n_splits, &splits, &len);
+  if (splits <= 1) return 0;
+  return (size_t)B * Hq * splits * (cb->d + 2) * sizeof(float);
+}
+
+kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                           const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
+                           int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
+                           void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
+                           void* stream) {
+  kvq::AttnParams p;
+  ReadShape rs;
+  kvq_status st = check_read(cb, signs, q, qdtype, codes, norms, B, Hq, Hkv, T_cap, &p, &rs);
+  if (st != KVQ_OK) return st;
+  if (!valid_dtype(vdtype) || !valid_dtype(odtype)) return fail(KVQ_ERR_INVALID_ARG, "bad v/out dtype");
+  if (!v || !out) return fail(KVQ_ERR_INVALID_ARG, "v or out is NULL");
+  if (!aligned16(v) || !aligned16(out)) return fail(KVQ_ERR_INVALID_ARG, "v or out not 16-byte aligned");
+  if (n_splits < 0) return fail(KVQ_ERR_INVALID_ARG, "n_splits=%d", n_splits);
+  if (!std::isfinite(scale)) return fail(KVQ_ERR_INVALID_ARG, "scale is not finite");
+  p.seq_lens = seq_lens;
+  p.v = v;
+  p.out = out;
+  p.out_f16 = odtype == KVQ_F16;
+  p.zscale = scale * 1.4426950408889634f;
+  choose_splits(rs.units, T_cap, n_splits, &p.n_splits, &p.split_len);
+  if (p.n_splits > 1) {
+    const size_t need = (size_t)B * Hq * p.n_splits * (cb->d + 2) * sizeof(float);
+    if (!workspace || ws_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    p.ws = reinterpret_cast<float*>(workspace);
+  }
+  const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = cb->kind == KVQ_HADAMARD_LM
+                     ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
+                     : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
+  if (e != hipSuccess) return from_hip(e, "kvq_decode_attn");
+  if (p.n_splits > 1) return from_hip(kvq::launch_combine(p, cb->d, s), "kvq_decode_attn combine");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device-side helpers for libkvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kvq {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int N> struct VecF;
+template <> struct VecF<1> { typedef float type; };
+template <> struct VecF<2> { typedef float2 type; };
+template <> struct VecF<4> { typedef float4 type; };
+
+__device__ __forceinline__ void add_into(float* acc, float e) { acc[0] += e; }
+__device__ __forceinline__ void add_into(float* acc, float2 e) { acc[0] += e.x; acc[1] += e.y; }
+__device__ __forceinline__ void add_into(float* acc, float4 e) {
+  acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
+}
+
+// Orders this wave's LDS writes before its later LDS reads (data exchanged
+// between lanes of one wave through LDS).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Load the N-byte code row at p (p aligned to the largest power of two <= 16
+// dividing N) into 32-bit words, little-endian.
+template <int N>
+__device__ __forceinline__ void load_code_row(const uint8_t* __restrict__ p, uint32_t (&w)[(N + 3) / 4]) {
+  if constexpr (N % 16 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 16; ++k) {
+      uint4 x = reinterpret_cast<const uint4*>(p)[k];
+      w[4 * k + 0] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
+    }
+  } else if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 8; ++k) {
+      uint2 x = reinterpret_cast<const uint2*>(p)[k];
+      w[2 * k + 0] = x.x; w[2 * k + 1] = x.y;
+    }
+  } else if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) w[k] = reinterpret_cast<const uint32_t*>(p)[k];
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int k = 0; k < (N + 3) / 4; ++k) w[k] = 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) w[k / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(p)[k] << (16 * (k % 2));
+  } else {
+#pragma unroll
+    for (int k = 0; k < (N + 3) / 4; ++k) w[k] = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) w[k / 4] |= (uint32_t)p[k] << (8 * (k % 4));
+  }
+}
+
+// Bits [I*B, I*B+B) of a little-endian word array (I, B compile-time).
+template <int I, int B, int NW>
+__device__ __forceinline__ uint32_t bit_field(const uint32_t (&w)[NW]) {
+  constexpr int bit = I * B;
+  constexpr int word = bit / 32;
+  constexpr int off = bit % 32;
+  constexpr uint32_t mask = (1u << B) - 1u;
+  if constexpr (off + B <= 32) {
+    return (w[word] >> off) & mask;
+  } else {
+    return ((w[word] >> off) | (w[word + 1] << (32 - off))) & mask;
+  }
+}
+
+// fp16 <-> fp32 helpers on raw bits.
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+}  // namespace kvq

@@ -1,0 +1,66 @@
+// Internal declarations shared by the host API and the kernel translation units
+// of libkvq.  Not installed; the public interface is include/kvq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kvq {
+
+// Everything a read-path kernel needs, passed by value as the kernel argument.
+struct AttnParams {
+  const void* q;             // [B][Hq][D] fp16 or fp32
+  const uint8_t* codes;      // [B][Hkv][T_cap][bytes per key]
+  const float* norms;        // [B][Hkv][T_cap] (Hadamard/Lloyd-Max only)
+  const void* v;             // [B][Hkv][T_cap][D] fp16 or fp32
+  const int32_t* seq_lens;   // [B] or nullptr (= T_cap)
+  const float* pq_cent;      // [Hkv][M][K][D/M] (PQ only)
+  float* scores;             // score kernel output [B][Hq][T_cap]
+  float* ws;                 // split partials [B][Hq][n_splits][D+2]
+  void* out;                 // [B][Hq][D] fp16 or fp32
+  int64_t T_cap;
+  int64_t split_len;         // tokens per split (multiple of 64)
+  int B, Hq, Hkv, G;         // G = Hq / Hkv
+  int n_groups;              // G / heads-per-workgroup
+  int n_splits;
+  int q_f16, out_f16;
+  int pq_K;
+  float zscale;              // softmax scale * log2(e)
+  float levels[16];
+  uint32_t signs[8];         // bit i set <=> coordinate i is negated
+};
+
+struct EncodeParams {
+  const void* keys;          // [B][Hkv][T_new][D]
+  uint8_t* codes;            // [B][Hkv][T_cap][bytes per key]
+  float* norms;              // [B][Hkv][T_cap]
+  const int32_t* write_pos;  // [B] or nullptr
+  const float* pq_cent;      // PQ only
+  int64_t T_new, T_cap, t0;
+  int B, Hkv;
+  int pq_K;
+  float thresholds[15];
+  uint32_t signs[8];
+};
+
+// Kernel launchers.  Each returns hipSuccess or the launch error; an
+// unsupported template combination returns hipErrorNotSupported without
+// launching.  heads_per_wg is the number of query heads one workgroup serves.
+hipError_t launch_hlm_decode(int D, int bits, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
+                             hipStream_t s);
+hipError_t launch_hlm_score(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_pq_decode(int D, int M, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
+                            hipStream_t s);
+hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_combine(const AttnParams& p, int D, hipStream_t s);
+hipError_t launch_hlm_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
+hipError_t launch_pq_encode(int D, int M, bool k_f16, const EncodeParams& p, hipStream_t s);
+
+// Host codebook construction (codebook.cpp).
+void lloyd_max_gaussian(int b, double* levels, double* thresholds);
+void kmeans_lloyd(const float* train, int64_t n, int dim, int stride, int K, int iters, const int64_t* start,
+                  double* cent);
+
+}  // namespace kvq

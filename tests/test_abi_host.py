@@ -1,0 +1,167 @@
+"""CPU checks of the library's host side: it loads, exports every symbol the
+header declares, builds the same codebooks as the oracle, and rejects bad
+arguments before launching anything (fake, never-dereferenced pointers are
+used only where validation must fail first)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    from quantized_kv_cache_encode_amd import build
+    if build.is_stale():
+        build.build()
+    import quantized_kv_cache_encode_amd.kvq as kvq
+    return kvq
+
+
+def test_exports_every_declared_symbol(K):
+    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kvq_[a-z_0-9]+)\s*\(", hdr, flags=re.M))
+    assert declared >= {"kvq_build_codebook", "kvq_encode_keys", "kvq_score", "kvq_decode_attn"}
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(K.EXPORTS)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_codebook_matches_oracle(K, oracle_mod, d, b):
+    cb = K.kvq_build_codebook(d, b)
+    lv, th = oracle_mod.codebook(d, b)
+    np.testing.assert_array_equal(cb.levels_array(), lv.astype(np.float32))
+    np.testing.assert_array_equal(cb.thresholds_array(), th.astype(np.float32))
+    assert cb.kind == K.KVQ_HADAMARD_LM and cb.d == d and cb.b == b
+
+
+def test_pq_kmeans_matches_oracle(K, oracle_mod):
+    sh = W.scaled(W.PQ_GPT2, Hkv=2, Hq=2, K=64)
+    train = W.pq_training(sh, n_train=1024)
+    start = W.pq_start_rows(sh, n_train=1024)
+    cent = K.kvq_build_codebook_pq(train, sh.m, sh.K, 10, start)
+    ds = sh.d // sh.m
+    for h in range(sh.Hkv):
+        for s in range(sh.m):
+            ref, _ = oracle_mod.kmeans(train[h][:, s * ds:(s + 1) * ds], sh.K, 10, start[h, s])
+            np.testing.assert_allclose(cent[h, s], ref, rtol=1e-6, atol=1e-6)
+
+
+def test_version_and_last_error(K):
+    assert K.kvq_version() >= 100
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_build_codebook(48, 4)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    assert "d=48" in K.kvq_last_error()
+    K.kvq_build_codebook(64, 4)
+    assert K.kvq_last_error() == ""
+
+
+@pytest.mark.parametrize("d,b", [(8, 2), (24, 2), (512, 4), (64, 0), (64, 5)])
+def test_codebook_rejects(K, d, b):
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_build_codebook(d, b)
+    assert e.value.status == K.KVQ_ERR_INVALID_ARG
+
+
+FAKE = 0x100000  # aligned, never dereferenced: every call below must fail validation first
+
+
+def _raw(K):
+    return ctypes.CDLL(K.LIB_PATH)
+
+
+def _call_encode(K, cb, signs, keys=FAKE, kdt=1, B=1, H=1, T_new=4, codes=FAKE, norms=FAKE, T_cap=64, t0=0, wp=None):
+    lib = K._lib
+    s = None if signs is None else np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+    return lib.kvq_encode_keys(ctypes.byref(cb), None if s is None else s.ctypes.data_as(ctypes.c_void_p),
+                               ctypes.c_void_p(keys), kdt, B, H, T_new, ctypes.c_void_p(codes),
+                               None if norms is None else ctypes.c_void_p(norms), T_cap, t0,
+                               None if wp is None else ctypes.c_void_p(wp), None)
+
+
+def test_encode_validation(K):
+    cb = K.kvq_build_codebook(16, 2)
+    ok_signs = np.ones(16, dtype=np.int8)
+    bad = np.ones(16, dtype=np.int8)
+    bad[3] = 0
+    assert _call_encode(K, cb, bad) == K.KVQ_ERR_INVALID_ARG
+    assert "signs[3]" in K.kvq_last_error()
+    assert _call_encode(K, cb, None) == K.KVQ_ERR_INVALID_ARG
+    assert _call_encode(K, cb, ok_signs, keys=FAKE + 2) == K.KVQ_ERR_INVALID_ARG          # misaligned
+    assert _call_encode(K, cb, ok_signs, codes=0) == K.KVQ_ERR_INVALID_ARG                # NULL codes
+    assert _call_encode(K, cb, ok_signs, norms=None) == K.KVQ_ERR_INVALID_ARG             # NULL norms
+    assert _call_encode(K, cb, ok_signs, kdt=7) == K.KVQ_ERR_INVALID_ARG                  # dtype
+    assert _call_encode(K, cb, ok_signs, T_cap=0) == K.KVQ_ERR_INVALID_ARG
+    assert _call_encode(K, cb, ok_signs, t0=62, T_new=4) == K.KVQ_ERR_INVALID_ARG         # does not fit
+    assert _call_encode(K, cb, ok_signs, t0=-1) == K.KVQ_ERR_INVALID_ARG
+    assert _call_encode(K, cb, ok_signs, B=0) == K.KVQ_ERR_INVALID_ARG
+    bad_cb = K.kvq_build_codebook(16, 2)
+    bad_cb.b = 5
+    assert _call_encode(K, bad_cb, ok_signs) == K.KVQ_ERR_INVALID_ARG
+    bad_cb.b, bad_cb.d = 2, 20
+    assert _call_encode(K, bad_cb, ok_signs) == K.KVQ_ERR_INVALID_ARG
+    bad_cb.kind = 9
+    assert _call_encode(K, bad_cb, ok_signs) == K.KVQ_ERR_INVALID_ARG
+
+
+def _call_decode(K, cb, signs, B=1, Hq=4, Hkv=2, T_cap=4096, ws=FAKE, ws_bytes=0, n_splits=0, q=FAKE, scale=0.25,
+                 vdt=1, odt=1):
+    lib = K._lib
+    s = np.ascontiguousarray(np.asarray(signs, dtype=np.int8))
+    P = ctypes.c_void_p
+    return lib.kvq_decode_attn(ctypes.byref(cb), s.ctypes.data_as(P), P(q), 1, P(FAKE), P(FAKE), P(FAKE), vdt, B,
+                               Hq, Hkv, T_cap, None, scale, P(FAKE), odt, None if ws is None else P(ws), ws_bytes,
+                               n_splits, None)
+
+
+def test_decode_validation_and_workspace(K):
+    cb = K.kvq_build_codebook(64, 4)
+    s = np.ones(64, dtype=np.int8)
+    assert _call_decode(K, cb, s, Hq=3, Hkv=2) == K.KVQ_ERR_INVALID_ARG       # Hq % Hkv
+    assert _call_decode(K, cb, s, T_cap=0) == K.KVQ_ERR_INVALID_ARG
+    assert _call_decode(K, cb, s, q=FAKE + 8) == K.KVQ_ERR_INVALID_ARG
+    assert _call_decode(K, cb, s, vdt=5) == K.KVQ_ERR_INVALID_ARG
+    assert _call_decode(K, cb, s, n_splits=-1) == K.KVQ_ERR_INVALID_ARG
+    assert _call_decode(K, cb, s, scale=float("nan")) == K.KVQ_ERR_INVALID_ARG
+    need = K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 0)
+    assert need > 0
+    assert _call_decode(K, cb, s, ws=None, ws_bytes=0) == K.KVQ_ERR_WORKSPACE
+    assert _call_decode(K, cb, s, ws_bytes=need - 1) == K.KVQ_ERR_WORKSPACE
+    assert "workspace" in K.kvq_last_error()
+    # one split needs no workspace
+    assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 64, 0) == 0
+    assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 1) == 0
+    # workspace grows with the requested split count, and is 0 for invalid shapes
+    assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 64) == 1 * 4 * 64 * 66 * 4
+    assert K.kvq_decode_attn_workspace(cb, 1, 3, 2, 4096, 0) == 0
+
+
+def test_score_validation(K):
+    cb = K.kvq_build_codebook(64, 4)
+    s = np.ones(64, dtype=np.int8)
+    P = ctypes.c_void_p
+    lib = K._lib
+    # NULL scores
+    assert lib.kvq_score(ctypes.byref(cb), s.ctypes.data_as(P), P(FAKE), 1, P(FAKE), P(FAKE), 1, 4, 2, 128, None,
+                         None, None) == K.KVQ_ERR_INVALID_ARG
+    # NULL norms for the Hadamard codec
+    assert lib.kvq_score(ctypes.byref(cb), s.ctypes.data_as(P), P(FAKE), 1, P(FAKE), None, 1, 4, 2, 128, None,
+                         P(FAKE), None) == K.KVQ_ERR_INVALID_ARG
+
+
+def test_pq_codebook_validation(K):
+    with pytest.raises(K.KvqError):
+        K._check(K._lib.kvq_codebook_pq(64, 7, 256, 12, ctypes.c_void_p(FAKE), ctypes.byref(K.kvq_codebook())))
+    with pytest.raises(K.KvqError):
+        K._check(K._lib.kvq_codebook_pq(64, 8, 300, 12, ctypes.c_void_p(FAKE), ctypes.byref(K.kvq_codebook())))
+    with pytest.raises(K.KvqError):
+        K.kvq_build_codebook_pq(np.zeros((1, 10, 8), np.float32), 2, 4, 3, np.full((1, 2, 4), 11))
