@@ -167,7 +167,12 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
  *   out:      device [B][Hq][d], dtype odtype, written.  A sequence of
  *             length 0 gives zeros.
  *   workspace: device, at least kvq_decode_attn_workspace(...) bytes with the
- *             same n_splits; contents on entry are ignored.
+ *             same n_splits (may be NULL when that size is 0).  Its first
+ *             bytes are arrival counters that must be zero before the first
+ *             call using this workspace (allocate it zero-filled); every
+ *             completed call leaves them zero again, so the workspace can be
+ *             reused by later calls ordered on the device without clearing.
+ *             Calls that share a workspace concurrently race.
  *   n_splits: 0 = library's choice; otherwise 1..T_cap/64 rounded up (the
  *             result is the same up to rounding for every n_splits).
  * Errors: as kvq_encode_keys, plus KVQ_ERR_WORKSPACE. */

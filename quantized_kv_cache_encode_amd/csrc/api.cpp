@@ -8,7 +8,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace {
@@ -80,20 +80,31 @@ int heads_per_wg(int G) {
   return 1;
 }
 
+// Compute units of the current device (256 on MI355X; also the fallback when
+// no device can be queried, so that workspace sizes stay well defined).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
 // Split of the token axis: every split is a multiple of 64 tokens.  With no
-// request, aim for about 1024 workgroups (four per compute unit) but keep at
-// least 256 tokens (one chunk per wave) in a split.
+// request, aim for two workgroups per compute unit (one round of the grid)
+// but keep at least 256 tokens (one chunk per wave) in a split.
 void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len) {
   const int64_t max_splits = (T_cap + 63) / 64;
   int64_t s;
   if (requested > 0) {
     s = requested < max_splits ? requested : max_splits;
   } else {
-    s = (1024 + units - 1) / units;
+    const int64_t target = 2 * (int64_t)device_cus();
+    s = (target + units - 1) / units;
     const int64_t cap = (T_cap + 255) / 256;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
   }
+  if (s > 256) s = 256;  // the split merge keeps per-split scalars of a unit in LDS
   int64_t len = (T_cap + s - 1) / s;
   len = (len + 63) / 64 * 64;
   *split_len = len;
@@ -145,6 +156,15 @@ kvq_status check_read(const kvq_codebook* cb, const int8_t* signs, const void* q
   p->G = G;
   p->n_groups = rs->n_groups;
   return KVQ_OK;
+}
+
+// Workspace of a split decode: arrival counters (4 bytes per unit, padded to
+// 256 bytes) followed by the fp32 partials [B][Hq][splits][d+4] (d accumulators,
+// the running maximum and the sum, padded).
+size_t workspace_bytes(int64_t units, int B, int Hq, int splits, int d) {
+  if (splits <= 1) return 0;
+  const size_t counters = ((size_t)units * 4 + 255) / 256 * 256;
+  return counters + (size_t)B * Hq * splits * (d + 4) * sizeof(float);
 }
 
 }  // namespace
@@ -272,11 +292,11 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
     return 0;
   const int G = Hq / Hkv;
   const int gg = heads_per_wg(G);
+  const int64_t units = (int64_t)B * Hkv * (G / gg);
   int splits;
   int64_t len;
-  choose_splits((int64_t)B * Hkv * (G / gg), T_cap, n_splits, &splits, &len);
-  if (splits <= 1) return 0;
-  return (size_t)B * Hq * splits * (cb->d + 2) * sizeof(float);
+  choose_splits(units, T_cap, n_splits, &splits, &len);
+  return workspace_bytes(units, B, Hq, splits, cb->d);
 }
 
 kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
@@ -300,20 +320,20 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
   p.zscale = scale * 1.4426950408889634f;
   choose_splits(rs.units, T_cap, n_splits, &p.n_splits, &p.split_len);
   if (p.n_splits > 1) {
-    const size_t need = (size_t)B * Hq * p.n_splits * (cb->d + 2) * sizeof(float);
+    const size_t need = workspace_bytes(rs.units, B, Hq, p.n_splits, cb->d);
     if (!workspace || ws_bytes < need)
       return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
     if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-    p.ws = reinterpret_cast<float*>(workspace);
+    const size_t counter_bytes = ((size_t)rs.units * 4 + 255) / 256 * 256;
+    p.counters = reinterpret_cast<unsigned*>(workspace);
+    p.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counter_bytes);
   }
   const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = cb->kind == KVQ_HADAMARD_LM
                      ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
                      : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
-  if (e != hipSuccess) return from_hip(e, "kvq_decode_attn");
-  if (p.n_splits > 1) return from_hip(kvq::launch_combine(p, cb->d, s), "kvq_decode_attn combine");
-  return ok();
+  return from_hip(e, "kvq_decode_attn");
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@ struct AttnParams {
   const float* pq_cent;      // [Hkv][M][K][D/M] (PQ only)
   float* scores;             // score kernel output [B][Hq][T_cap]
   float* ws;                 // split partials [B][Hq][n_splits][D+2]
+  unsigned* counters;        // [units] arrival counters of the split merge (zero between calls)
   void* out;                 // [B][Hq][D] fp16 or fp32
   int64_t T_cap;
   int64_t split_len;         // tokens per split (multiple of 64)
@@ -54,7 +55,6 @@ hipError_t launch_hlm_score(int D, int bits, int heads_per_wg, const AttnParams&
 hipError_t launch_pq_decode(int D, int M, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
                             hipStream_t s);
 hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
-hipError_t launch_combine(const AttnParams& p, int D, hipStream_t s);
 hipError_t launch_hlm_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
 hipError_t launch_pq_encode(int D, int M, bool k_f16, const EncodeParams& p, hipStream_t s);
 

@@ -207,7 +207,7 @@ def kvq_decode_attn(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tenso
         out = torch.empty((B, Hq, d), dtype=out_dtype or v.dtype, device=q.device)
     need = kvq_decode_attn_workspace(cb, B, Hq, Hkv, T_cap, n_splits)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
     ws_ptr = _dev(workspace, "workspace", optional=True)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     s_np, s_ptr = _signs_host(signs, d)

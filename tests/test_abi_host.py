@@ -141,7 +141,7 @@ def test_decode_validation_and_workspace(K):
     assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 64, 0) == 0
     assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 1) == 0
     # workspace grows with the requested split count, and is 0 for invalid shapes
-    assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 64) == 1 * 4 * 64 * 66 * 4
+    assert K.kvq_decode_attn_workspace(cb, 1, 4, 2, 4096, 64) == 256 + 1 * 4 * 64 * (64 + 4) * 4  # counters + partials
     assert K.kvq_decode_attn_workspace(cb, 1, 3, 2, 4096, 0) == 0
 
 
