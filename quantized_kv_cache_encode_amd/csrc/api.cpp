@@ -90,17 +90,18 @@ int device_cus() {
 }
 
 // Split of the token axis: every split is a multiple of 64 tokens.  With no
-// request, aim for two workgroups per compute unit (one round of the grid)
-// but keep at least 256 tokens (one chunk per wave) in a split.
+// request, aim for one workgroup per compute unit (one round of the grid) but
+// keep at least one 64-token chunk per wave in a split.
 void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len) {
   const int64_t max_splits = (T_cap + 63) / 64;
   int64_t s;
   if (requested > 0) {
     s = requested < max_splits ? requested : max_splits;
   } else {
-    const int64_t target = 2 * (int64_t)device_cus();
+    const int64_t target = (int64_t)device_cus();
     s = (target + units - 1) / units;
-    const int64_t cap = (T_cap + 255) / 256;
+    const int64_t min_tokens = kvq::kReadThreads;  // 64 tokens for each of the workgroup's waves
+    const int64_t cap = (T_cap + min_tokens - 1) / min_tokens;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
   }

@@ -10,7 +10,7 @@
 // Shift-accumulate attention page (English abstract): decode attention fused
 // with an online softmax.
 //
-// Work decomposition (one workgroup = 4 waves of 64 lanes):
+// Work decomposition (one workgroup = 8 waves of 64 lanes):
 //   workgroup <- (batch b, kv head, group of GG query heads, split of T);
 //   prologue: the GG queries are loaded into LDS, sign-flipped and put
 //   through an in-LDS fast Walsh-Hadamard transform (Hadamard codec), then
@@ -28,7 +28,7 @@
 //   more than 2^8 (so probabilities stay <= 256), and the probabilities are
 //   staged through LDS as the B operand of MFMA 16x16x16 f16 (fp32 values:
 //   16x16x4 f32) whose A operand is V^T, giving out^T[dim][head] in the
-//   matrix-core accumulators.  The four waves merge their (max, sum, acc)
+//   matrix-core accumulators.  The waves merge their (max, sum, acc)
 //   through LDS; the splits of one (b, kv head, head group) are merged by
 //   the last of its workgroups to finish (log-sum-exp merge), found with an
 //   arrival counter in the workspace that the last workgroup resets to zero.
@@ -41,7 +41,7 @@
 
 namespace kvq {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kReadThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 64;
 constexpr float kLazyHeadroom = 8.0f;  // log2 of the largest probability allowed before rescaling
@@ -166,31 +166,46 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 // codec every query is also rotated, q' = H D q / sqrt(d): 8 consecutive coordinates per lane and d/8
 // lanes per query, sign flip, then a radix-2 fast Walsh-Hadamard transform (Sylvester order) in registers
 // (distances 1, 2, 4) and across the query's lanes (distances 8 .. d/2).
-template <class S, int GG>
-__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* lv, uint32_t*, int tid) {
+// `between` runs after this thread's query loads are issued and before they are used: the caller issues
+// its first cache loads there, so they are in flight during the rotation and the table build (vector
+// memory loads complete in order, so waiting for the query does not wait for them).
+template <class S, int GG, class F>
+__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
   if (tid < 16) lv[tid] = p.levels[tid];
   if constexpr (S::kRotate) {
     constexpr int LPQ = D / 8;  // lanes per query (a power of two <= 32, so groups never straddle waves)
     static_assert(GG * LPQ <= kThreads, "one lane per 8 coordinates of every query");
     const int g = tid / LPQ, k = tid % LPQ;
+    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + 8 * k;
+    const uint32_t sb = (p.signs[(8 * k) >> 5] >> ((8 * k) & 31)) & 0xffu;
+    uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
     if (g < GG) {
-      const size_t off = ((size_t)u.b * p.Hq + u.h0 + g) * D + 8 * k;
+      if (p.q_f16) {
+        raw0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off);
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + off);
+        raw0 = src[0];
+        raw1 = src[1];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+    if (g < GG) {
       float x[8];
       if (p.q_f16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off);
-        const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t r[4] = {raw0.x, raw0.y, raw0.z, raw0.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           x[2 * t] = h2f((uint16_t)(r[t] & 0xffffu));
           x[2 * t + 1] = h2f((uint16_t)(r[t] >> 16));
         }
       } else {
-        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.q) + off);
-        const float4 a = src[0], b = src[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        const uint32_t r[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = __builtin_bit_cast(float, r[t]);
       }
-      const uint32_t sb = (p.signs[(8 * k) >> 5] >> ((8 * k) & 31)) & 0xffu;
 #pragma unroll
       for (int t = 0; t < 8; ++t)
         if ((sb >> t) & 1u) x[t] = -x[t];
@@ -217,12 +232,13 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* l
       for (int t = 0; t < 8; ++t) qs[g * D + 8 * k + t] = x[t] * rs;
     }
   } else {
+    between();
     for (int idx = tid; idx < GG * D; idx += kThreads) {
       const size_t off = ((size_t)u.b * p.Hq + u.h0 + idx / D) * D + idx % D;
       qs[idx] = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off] : reinterpret_cast<const float*>(p.q)[off];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Scores of the key held by this lane for all GG heads (before the norm).
@@ -238,25 +254,38 @@ __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut
   for (int g = 0; g < GG; ++g) acc[g] = 0.0f;
   if constexpr (S::kNibbles) {
     // Two 4-bit codes per byte: shift every nibble into place as a byte offset (code * ES) so that one
-    // byte extract gives the LDS address of a coordinate's entry.
+    // byte extract gives the LDS address of a coordinate's entry.  The gathers run one stage (4
+    // coordinates x NQ head groups) ahead of the adds that consume them, so 2*4*NQ reads are in flight;
+    // the scheduling barriers keep the compiler from folding the stages back together.
     constexpr int LG = ES == 16 ? 4 : (ES == 8 ? 3 : 2);
     constexpr uint32_t MASK = 0x0F0F0F0Fu << LG;
+    constexpr int ST = 4;                     // coordinates per stage
+    constexpr int NST = S::ROWS / ST;
+    E buf[2][ST * NQ];
+    auto issue = [&](int st, E* b) {
+      const int k = st / 2, half = st % 2;
+      const uint32_t e = (w[k] << LG) & MASK;        // even coordinates of word k
+      const uint32_t o = (w[k] >> (4 - LG)) & MASK;  // odd coordinates of word k
 #pragma unroll
-    for (int k = 0; k < S::NW; ++k) {
-      const uint32_t e = (w[k] << LG) & MASK;        // even coordinates
-      const uint32_t o = (w[k] >> (4 - LG)) & MASK;  // odd coordinates
+      for (int cc = 0; cc < ST; ++cc) {
+        const int m = 2 * half + cc / 2;
+        const uint32_t a = __builtin_amdgcn_ubfe(cc % 2 ? o : e, 8 * m, 8);
+        const int i = ST * st + cc;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int i0 = 8 * k + 2 * m;
-        const uint32_t ae = (e >> (8 * m)) & 0xFFu;
-        const uint32_t ao = (o >> (8 * m)) & 0xFFu;
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) {
-          add_into(acc + qq * HW, *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i0) * S::COLS) * ES + ae));
-          add_into(acc + qq * HW,
-                   *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i0 + 1) * S::COLS) * ES + ao));
-        }
+        for (int qq = 0; qq < NQ; ++qq)
+          b[cc * NQ + qq] = *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i) * S::COLS) * ES + a);
       }
+    };
+    issue(0, buf[0]);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + 1 < NST) issue(st + 1, buf[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int cc = 0; cc < ST; ++cc)
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) add_into(acc + qq * HW, buf[st & 1][cc * NQ + qq]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
 #pragma unroll
@@ -351,7 +380,7 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 }
 
 template <class S, int GG, bool VF16>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(const AttnParams p) {
   constexpr int D = S::D;
   constexpr int DPL = D / 16;  // V columns per lane per MFMA tile set
   using Plan = LdsPlan<S, GG>;
@@ -360,7 +389,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const AttnParams p) {
   typedef PT vrow_t __attribute__((ext_vector_type(DPL < 2 ? 2 : DPL)));
   __shared__ __align__(16) unsigned char smem[Plan::total(VF16)];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
-  uint32_t* sg = reinterpret_cast<uint32_t*>(smem + Plan::consts_off + 64);
   int* s_flag = reinterpret_cast<int*>(smem + Plan::consts_off + 96);
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
   PT* pst = reinterpret_cast<PT*>(smem + Plan::pst_off);
@@ -403,11 +431,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const AttnParams p) {
           vn[ks][s] = load_vrow_buf<PT, DPL, vrow_t>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT));
     }
   };
-  if (c < n_valid) fetch(c);
-
-  prologue<S, GG>(p, u, qs, lv, sg, tid);
+  // (loads past the split's end read as zeros, so the fetches need no guard: a guard would also make the
+  // compiler wait for every outstanding load wherever it cannot count them)
+  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c); });
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
-  __syncthreads();
+  lds_barrier();
 
   float m_run[GG], l_lane[GG];
 #pragma unroll
@@ -420,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const AttnParams p) {
   for (int j = 0; j < DPL; ++j) oacc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
   PT* pw = pst + wid * GG * kChunk;
 
+#pragma unroll 2
   for (; c < n_valid; c += kWaves * kChunk) {
     // this chunk's data (fetched one iteration earlier), then the next chunk's requests
     uint32_t w[S::NW];
@@ -431,14 +460,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const AttnParams p) {
     for (int ks = 0; ks < KS16; ++ks)
 #pragma unroll
       for (int s = 0; s < 4; ++s) vr[ks][s] = vn[ks][s];
-    if (c + kWaves * kChunk < n_valid) fetch(c + kWaves * kChunk);
+    fetch(c + kWaves * kChunk);
 
     // ---- scores from the table
     float acc[GG];
     lut_scores<S, GG>(smem, w, acc);
     float z[GG];
+    const float zs = S::kNorm ? nrm * p.zscale : p.zscale;
 #pragma unroll
-    for (int g = 0; g < GG; ++g) z[g] = (S::kNorm ? nrm * acc[g] : acc[g]) * p.zscale;
+    for (int g = 0; g < GG; ++g) z[g] = acc[g] * zs;
     if (c + kChunk > n_valid) {  // the split's last, partial chunk
       const bool valid = c + lane < n_valid;
 #pragma unroll
@@ -603,7 +633,6 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const AttnParams p) {
   constexpr int HW = Plan::HW;
   __shared__ __align__(16) unsigned char smem[Plan::pst_off];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
-  uint32_t* sg = reinterpret_cast<uint32_t*>(smem + Plan::consts_off + 64);
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -620,9 +649,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const AttnParams p) {
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(S::kNorm ? (const void*)(p.norms + rowb) : (const void*)p.codes,
                                               S::kNorm ? (int64_t)n_valid * 4 : 0);
 
-  prologue<S, GG>(p, u, qs, lv, sg, tid);
+  prologue<S, GG>(p, u, qs, lv, tid, [] {});
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
-  __syncthreads();
+  lds_barrier();
 
   for (int c = wid * kChunk; c < n_stop; c += kWaves * kChunk) {
     uint32_t w[S::NW];

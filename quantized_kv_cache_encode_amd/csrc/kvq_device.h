@@ -23,6 +23,15 @@ __device__ __forceinline__ void add_into(float* acc, float4 e) {
   acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
 }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for this wave's outstanding global-memory loads, so prefetches
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Orders this wave's LDS writes before its later LDS reads (data exchanged
 // between lanes of one wave through LDS).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

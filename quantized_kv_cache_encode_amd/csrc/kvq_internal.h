@@ -9,6 +9,10 @@
 
 namespace kvq {
 
+// Threads of a read-path workgroup (8 waves of 64): one workgroup per compute unit
+// keeps two waves on each SIMD.
+constexpr int kReadThreads = 512;
+
 // Everything a read-path kernel needs, passed by value as the kernel argument.
 struct AttnParams {
   const void* q;             // [B][Hq][D] fp16 or fp32

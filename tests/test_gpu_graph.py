@@ -1,0 +1,58 @@
+"""The write + read path captured in a HIP graph and replayed: every replay must equal the eager result.
+
+Replays are interleaved with the program's own eager work and synchronizations, and the split-merge
+arrival counters (which each call leaves at zero) are exercised across replays.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import log, torch_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    import torch
+    import quantized_kv_cache_encode_amd.kvq as K
+
+    shape = W.scaled(W.LONGCTX, B=2, T=3000)  # several splits per (b, kv head) and a ragged tail
+    signs = W.signs(shape)
+    cb = K.kvq_build_codebook(shape.d, shape.b)
+    keys = torch_dev(W.keys(shape))
+    q = torch_dev(W.queries(shape))
+    v = torch_dev(W.values(shape))
+    newk = torch_dev(W.new_keys(shape))
+    B, Hq, Hkv, d, T = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T
+    codes = torch.zeros((B, Hkv, T, cb.bytes_per_key), dtype=torch.uint8, device="cuda:0")
+    norms = torch.zeros((B, Hkv, T), dtype=torch.float32, device="cuda:0")
+    K.kvq_encode_keys(cb, signs, keys, codes, norms)
+    ws = torch.zeros(K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, 0), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty((B, Hq, d), dtype=torch.float16, device="cuda:0")
+
+    def step():
+        K.kvq_encode_keys(cb, signs, newk, codes, norms, t0=T - 1)
+        K.kvq_decode_attn(cb, signs, q, codes, norms, v, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    eager_codes = codes.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        junk = torch.randn(1 << 20, device="cuda:0").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("replay %d: junk %.3f" % (r, float(junk)))
+        assert torch.equal(out, eager), "replay %d differs from the eager result" % r
+        assert torch.equal(codes, eager_codes)
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "arrival counters not left at zero"
