@@ -28,6 +28,40 @@ sys.path.insert(0, ROOT)
 
 METRIC = "keys scored/sec and % of HBM roofline, fused 4-bit LUT decode attn, B=8 T=32k"
 HBM_PEAK_GBS = 8000.0
+# Measured HBM traffic of the decode-attention kernel on this workload (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# passes, scaled by a plain copy of known size).  It is reported only while the library sources hash to
+# the digest recorded with the counters; after any change to them the figure is stale and traffic is null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_longctx_hbm_traffic.txt")
+
+
+def library_source_digest():
+    """sha256 over the HIP/C++ sources and headers of libkvq (names and contents, sorted by name)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_encode_amd", "csrc")
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".h", ".hip", ".cpp")))
+    for f in files + ["kvq.h"]:
+        path = os.path.join(ROOT, "include", f) if f == "kvq.h" else os.path.join(csrc, f)
+        h.update(f.encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != library_source_digest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def eprint(*a):
@@ -173,6 +207,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     attn_avg_ms = a_start.elapsed_time(a_stop) / a.steps
 
+    if a.calibrate_copy:
+        # a plain device-to-device copy of known size: 256 MiB read + 256 MiB written per launch
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     key_scores = B * Hq * T
     value = key_scores / (ms_per_step * 1e-3)
     alg_bytes = algorithmic_bytes(shape, bpk)
@@ -207,7 +250,7 @@ def main(argv=None):
                    "step": "encode B*Hkv new keys + fused decode attention over T keys",
                    "caches_rotated": len(caches), "t_splits": int(splits_used)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "decode_kernel (fused LUT score + online softmax + AV + split merge)",
                      "avg_launch_ms": attn_avg_ms, "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,

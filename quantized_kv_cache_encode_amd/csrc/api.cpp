@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -126,6 +127,9 @@ kvq_status check_read(const kvq_codebook* cb, const int8_t* signs, const void* q
   if (Hq % Hkv != 0) return fail(KVQ_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (T_cap <= 0) return fail(KVQ_ERR_INVALID_ARG, "T_cap=%lld must be positive", (long long)T_cap);
   if ((int64_t)B * Hkv > 65535 * 8) return fail(KVQ_ERR_INVALID_ARG, "B*Hkv too large");
+  // the kernels address a split's codes, norms and V and a unit's score rows with 32-bit byte offsets
+  if (T_cap >= (((int64_t)1 << 31) / (4 * (int64_t)std::max(cb->d, 32))))
+    return fail(KVQ_ERR_UNSUPPORTED, "T_cap=%lld too large for d=%d (32-bit offsets)", (long long)T_cap, cb->d);
   if (!valid_dtype(qdtype)) return fail(KVQ_ERR_INVALID_ARG, "bad q dtype %d", (int)qdtype);
   if (!q || !codes) return fail(KVQ_ERR_INVALID_ARG, "q or codes is NULL");
   if (!aligned16(q) || !aligned16(codes)) return fail(KVQ_ERR_INVALID_ARG, "q or codes not 16-byte aligned");

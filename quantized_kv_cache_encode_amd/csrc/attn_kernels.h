@@ -73,22 +73,29 @@ struct HlmScorer {
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) { return code_at<BITS, NW>(w, i); }
   // LUT[g][i][j] = q'_{g,i} * c_j with q' = H D q / sqrt(d) held in qs; one HW-wide entry (HW heads) per
   // (head group, coordinate, level).
+  // Each work item fills JPT consecutive levels of one (head group, coordinate) row.
   template <int GG, int HW>
   __device__ static void build(const AttnParams&, const float* qs, const float* lv, float* lut, int, int tid) {
     using E = typename VecF<HW>::type;
-    constexpr int total = (GG / HW) * ROWS * COLS;
+    constexpr int JPT = COLS < 4 ? COLS : 4;
+    constexpr int NJ = COLS / JPT;
+    constexpr int total = (GG / HW) * ROWS * NJ;
     E* L = reinterpret_cast<E*>(lut);
     for (int e = tid; e < total; e += kThreads) {
-      const int j = e % COLS;
-      const int i = (e / COLS) % ROWS;
-      const int g0 = (e / (COLS * ROWS)) * HW;
-      const float c = lv[j];
-      float v[4];
+      const int j0 = (e % NJ) * JPT;
+      const int i = (e / NJ) % ROWS;
+      const int g0 = (e / (NJ * ROWS)) * HW;
+      float qv[HW];
 #pragma unroll
-      for (int h = 0; h < HW; ++h) v[h] = qs[(g0 + h) * D + i] * c;
-      if constexpr (HW == 4) L[e] = make_float4(v[0], v[1], v[2], v[3]);
-      else if constexpr (HW == 2) L[e] = make_float2(v[0], v[1]);
-      else L[e] = v[0];
+      for (int h = 0; h < HW; ++h) qv[h] = qs[(g0 + h) * D + i];
+      E* row = L + (size_t)(e / NJ) * COLS + j0;
+#pragma unroll
+      for (int jj = 0; jj < JPT; ++jj) {
+        const float c = lv[j0 + jj];
+        if constexpr (HW == 4) row[jj] = make_float4(qv[0] * c, qv[1] * c, qv[2] * c, qv[3] * c);
+        else if constexpr (HW == 2) row[jj] = make_float2(qv[0] * c, qv[1] * c);
+        else row[jj] = qv[0] * c;
+      }
     }
   }
 };
@@ -243,58 +250,79 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* l
 
 // Scores of the key held by this lane for all GG heads (before the norm).
 // `lut` is the byte address of the table in LDS.
+//
+// Every coordinate i contributes the table entry at (row i, column code_i) for each head group; its LDS
+// byte offset within the row is code_i * ES.  The gathers run one stage (4 coordinates x NQ head groups)
+// ahead of the adds that consume them, so 2*4*NQ reads are in flight; the scheduling barriers keep the
+// compiler from folding the stages back together (which would hold every gather of the key in registers).
+// The first stage initialises the sums.
 template <class S, int GG>
 __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut, const uint32_t (&w)[S::NW],
                                            float (&acc)[GG]) {
   constexpr int HW = GG < 4 ? GG : 4;
   constexpr int NQ = GG / HW;
   constexpr int ES = HW * 4;  // bytes per table entry
+  constexpr int LG = ES == 16 ? 4 : (ES == 8 ? 3 : 2);
+  constexpr uint32_t NMASK = 0xFu << LG;
   using E = typename VecF<HW>::type;
-#pragma unroll
-  for (int g = 0; g < GG; ++g) acc[g] = 0.0f;
-  if constexpr (S::kNibbles) {
-    // Two 4-bit codes per byte: shift every nibble into place as a byte offset (code * ES) so that one
-    // byte extract gives the LDS address of a coordinate's entry.  The gathers run one stage (4
-    // coordinates x NQ head groups) ahead of the adds that consume them, so 2*4*NQ reads are in flight;
-    // the scheduling barriers keep the compiler from folding the stages back together.
-    constexpr int LG = ES == 16 ? 4 : (ES == 8 ? 3 : 2);
-    constexpr uint32_t MASK = 0x0F0F0F0Fu << LG;
-    constexpr int ST = 4;                     // coordinates per stage
-    constexpr int NST = S::ROWS / ST;
-    E buf[2][ST * NQ];
-    auto issue = [&](int st, E* b) {
-      const int k = st / 2, half = st % 2;
-      const uint32_t e = (w[k] << LG) & MASK;        // even coordinates of word k
-      const uint32_t o = (w[k] >> (4 - LG)) & MASK;  // odd coordinates of word k
-#pragma unroll
-      for (int cc = 0; cc < ST; ++cc) {
-        const int m = 2 * half + cc / 2;
-        const uint32_t a = __builtin_amdgcn_ubfe(cc % 2 ? o : e, 8 * m, 8);
-        const int i = ST * st + cc;
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq)
-          b[cc * NQ + qq] = *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i) * S::COLS) * ES + a);
+  constexpr int ST = 4;  // coordinates per stage
+  static_assert(S::ROWS % ST == 0, "rows come in stages of four");
+  constexpr int NST = S::ROWS / ST;
+
+  // byte offset of coordinate i's entry within its row
+  auto col_offset = [&](int i) -> uint32_t {
+    if constexpr (S::kNibbles) {
+      // Two 4-bit codes per byte.  For the odd coordinate of byte m the offset is (w >> 8m) masked to the
+      // nibble's bits shifted by LG, for the even one the same with w shifted left by 4 first, so each
+      // address costs one masked byte extract (for ES = 16 a single byte-select AND).  The left shift is
+      // kept opaque so that the compiler does not merge it into the extracts.
+      const int k = i / 8, m = (i % 8) / 2;
+      uint32_t x;
+      if (i % 2) {
+        x = w[k] >> (4 - LG);
+      } else if constexpr (LG == 4) {
+        asm("v_lshlrev_b32 %0, 4, %1" : "=v"(x) : "v"(w[k]));
+      } else {
+        x = w[k] << LG;
       }
-    };
-    issue(0, buf[0]);
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      if (st + 1 < NST) issue(st + 1, buf[(st + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int cc = 0; cc < ST; ++cc)
-#pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) add_into(acc + qq * HW, buf[st & 1][cc * NQ + qq]);
-      __builtin_amdgcn_sched_barrier(0);
+      uint32_t a;
+      if (LG == 4 && m == 1)  // byte 1 under the mask in one byte-select AND (the compiler emits shift + AND)
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 src1_sel:DWORD"
+            : "=v"(a) : "v"(x), "s"(NMASK));
+      else
+        a = (m == 0 ? x : __builtin_amdgcn_ubfe(x, 8 * m, 8)) & NMASK;
+      return a;
+    } else {
+      return S::code(w, i) * (uint32_t)ES;
     }
-  } else {
+  };
+  E buf[2][ST * NQ];
+  auto issue = [&](int st, E* b) {
 #pragma unroll
-    for (int i = 0; i < S::ROWS; ++i) {
-      const uint32_t c = S::code(w, i);
+    for (int cc = 0; cc < ST; ++cc) {
+      const int i = ST * st + cc;
+      const uint32_t a = col_offset(i);
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
-        add_into(acc + qq * HW, reinterpret_cast<const E*>(lut)[(qq * S::ROWS + i) * S::COLS + c]);
+        b[cc * NQ + qq] = *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i) * S::COLS) * ES + a);
     }
+  };
+  issue(0, buf[0]);
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    if (st + 1 < NST) issue(st + 1, buf[(st + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int cc = 0; cc < ST; ++cc)
+#pragma unroll
+      for (int qq = 0; qq < NQ; ++qq) {
+        if (st == 0 && cc == 0) set_from(acc + qq * HW, buf[0][qq]);
+        else add_into(acc + qq * HW, buf[st & 1][cc * NQ + qq]);
+      }
+    // the stage's sums are materialised here: the compiler may not sink the adds past the later gathers
+#pragma unroll
+    for (int g = 0; g < GG; ++g) asm volatile("" : "+v"(acc[g]));
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -364,6 +392,40 @@ __device__ __forceinline__ VR load_vrow_buf(__amdgpu_buffer_rsrc_t r, int voff, 
   return out;
 }
 
+// The fp16 V slice of DPL consecutive elements at voff + soff as raw 32-bit words (element e in the low
+// (e even) or high (e odd) half of word e/2; a single element sits in the low half).  Past the split's
+// valid range the words read as 0.
+template <int DPL>
+__device__ __forceinline__ void load_vwords_f16(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                                uint32_t (&w)[DPL < 2 ? 1 : DPL / 2]) {
+  if constexpr (DPL == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+  } else if constexpr (DPL == 2) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  } else if constexpr (DPL == 4) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = x[0]; w[1] = x[1];
+  } else {
+    static_assert(DPL % 8 == 0, "V slice is a multiple of 16 bytes");
+#pragma unroll
+    for (int k = 0; k < DPL / 8; ++k) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, 0);
+      w[4 * k + 0] = x[0]; w[4 * k + 1] = x[1]; w[4 * k + 2] = x[2]; w[4 * k + 3] = x[3];
+    }
+  }
+}
+
+// Element j of four fp16 slices (rows 0..3) packed as the four halves of an MFMA operand.
+template <int VW>
+__device__ __forceinline__ half4_t gather_col_f16(const uint32_t (&r0)[VW], const uint32_t (&r1)[VW],
+                                                  const uint32_t (&r2)[VW], const uint32_t (&r3)[VW], int j) {
+  const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low halves of the two sources
+  const int k = j >> 1;
+  typedef unsigned u2 __attribute__((ext_vector_type(2)));
+  const u2 x = u2{__builtin_amdgcn_perm(r1[k], r0[k], sel), __builtin_amdgcn_perm(r3[k], r2[k], sel)};
+  return __builtin_bit_cast(half4_t, x);
+}
+
 // Arrival counter of one (b, kv head, head group): zero before the call, incremented once by every
 // split's workgroup (a single device-scope fetch-add: no retry loop, so late arrivals do not queue behind
 // each other), and put back to zero by the last one, which merges the splits.
@@ -412,28 +474,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const int voff_code = lane * S::BPK;
   const int voff_v = VF16 ? ((4 * kq) * D + DPL * r16) * (int)sizeof(PT) : (kq * D + DPL * r16) * (int)sizeof(PT);
 
-  // Loads run one chunk ahead of the arithmetic: the codes, norms and (fp16) V slices of chunk c+1 are
-  // requested before chunk c is scored.  The first chunk's are requested before the prologue so they
-  // arrive while the table is built.
-  constexpr int KS16 = VF16 ? 4 : 1;
-  int c = wid * kChunk;  // chunk start, relative to t_begin
-  uint32_t wn[S::NW];
-  float nn = 1.0f;
-  vrow_t vn[KS16][4];
-  auto fetch = [&](int cc) {
-    load_code_row_buf<S::BPK>(rc, voff_code, cc * S::BPK, wn);
-    if constexpr (S::kNorm) nn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, 0));
-    if constexpr (VF16) {
+  // Loads run one chunk (of this wave) ahead of the arithmetic: the codes and norms of the next chunk,
+  // and for d <= 64 its fp16 V slices, are requested before the current one is scored.  Two register sets
+  // alternate (the loop is unrolled by two), so nothing is copied between iterations and the wait for a
+  // chunk's data leaves the next chunk's requests in flight.  For d = 128 two chunks of V do not fit the
+  // register budget: a chunk's V is requested when the chunk starts and arrives behind its table
+  // gathers; for d = 256 four slices at a time are loaded just before their matrix products.  The first
+  // chunk's loads are requested before the prologue so they arrive while the table is built.  Loads past
+  // the split's end read as zeros, so the fetches need no guard (a guard would also make the compiler
+  // wait for every outstanding load wherever it cannot count them).
+  constexpr int STR = kWaves * kChunk;  // distance between a wave's consecutive chunks
+  constexpr int VW = DPL < 2 ? 1 : DPL / 2;  // 32-bit words per fp16 V slice
+  constexpr bool kVPre = VF16 && VW <= 2;
+  constexpr bool kVChunk = VF16 && VW == 4;
+  struct Chunk {
+    uint32_t w[S::NW];
+    float nrm;
+    uint32_t v[4][4][kVPre ? VW : 1];  // fp16 V slices as raw words, when prefetched
+  };
+  auto load_v = [&](int cc, int ks, uint32_t (&vb)[4][VW]) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+    for (int s = 0; s < 4; ++s) load_vwords_f16<DPL>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT), vb[s]);
+  };
+  auto fetch = [&](int cc, Chunk& k) {
+    load_code_row_buf<S::BPK>(rc, voff_code, cc * S::BPK, k.w);
+    k.nrm = 1.0f;
+    if constexpr (S::kNorm) k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, 0));
+    if constexpr (kVPre) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          vn[ks][s] = load_vrow_buf<PT, DPL, vrow_t>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT));
+      for (int ks = 0; ks < 4; ++ks) load_v(cc, ks, k.v[ks]);
     }
   };
-  // (loads past the split's end read as zeros, so the fetches need no guard: a guard would also make the
-  // compiler wait for every outstanding load wherever it cannot count them)
-  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c); });
+  int c = wid * kChunk;  // chunk start, relative to t_begin
+  Chunk ka, kb;
+  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c, ka); });
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   lds_barrier();
 
@@ -448,37 +522,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   for (int j = 0; j < DPL; ++j) oacc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
   PT* pw = pst + wid * GG * kChunk;
 
-#pragma unroll 2
-  for (; c < n_valid; c += kWaves * kChunk) {
-    // this chunk's data (fetched one iteration earlier), then the next chunk's requests
-    uint32_t w[S::NW];
+  // score one chunk (keys cc .. cc+63 of the split) and fold it into the softmax state and the output
+  auto process = [&](int cc, const Chunk& k) {
+    uint32_t vc[kVChunk ? 4 : 1][4][VW];  // d = 128: this chunk's V, requested before the gathers
+    if constexpr (kVChunk) {
 #pragma unroll
-    for (int k = 0; k < S::NW; ++k) w[k] = wn[k];
-    const float nrm = nn;
-    vrow_t vr[KS16][4];
-#pragma unroll
-    for (int ks = 0; ks < KS16; ++ks)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) vr[ks][s] = vn[ks][s];
-    fetch(c + kWaves * kChunk);
-
+      for (int ks = 0; ks < 4; ++ks) load_v(cc, ks, vc[ks]);
+    }
     // ---- scores from the table
     float acc[GG];
-    lut_scores<S, GG>(smem, w, acc);
+    lut_scores<S, GG>(smem, k.w, acc);
     float z[GG];
-    const float zs = S::kNorm ? nrm * p.zscale : p.zscale;
+    const float zs = S::kNorm ? k.nrm * p.zscale : p.zscale;
 #pragma unroll
     for (int g = 0; g < GG; ++g) z[g] = acc[g] * zs;
-    if (c + kChunk > n_valid) {  // the split's last, partial chunk
-      const bool valid = c + lane < n_valid;
+    if (cc + kChunk > n_valid) {  // the split's last, partial chunk
+      const bool valid = cc + lane < n_valid;
 #pragma unroll
       for (int g = 0; g < GG; ++g) z[g] = valid ? z[g] : -INFINITY;
     }
-    bool need = false;
+    // ---- online softmax: raise the running maximum only when some score exceeds it by the headroom
+    float rise = z[0] - m_run[0];
 #pragma unroll
-    for (int g = 0; g < GG; ++g) need |= z[g] > m_run[g] + kLazyHeadroom;
-    // ---- online softmax: raise the running maximum only when needed
-    if (__any(need)) {
+    for (int g = 1; g < GG; ++g) rise = fmaxf(rise, z[g] - m_run[g]);
+    if (__any(rise > kLazyHeadroom)) {
       float my_alpha = 1.0f;
 #pragma unroll
       for (int g = 0; g < GG; ++g) {
@@ -505,16 +572,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       for (int ks = 0; ks < 4; ++ks) {
         half4_t bop = half4_t{0, 0, 0, 0};
         if (r16 < GG) bop = *reinterpret_cast<const half4_t*>(pw + r16 * kChunk + 16 * ks + 4 * kq);
+        uint32_t vl[kVPre || kVChunk ? 1 : 4][VW];  // d = 256: four slices loaded here
+        if constexpr (!kVPre && !kVChunk) load_v(cc, ks, vl);
+        const auto& vb = [&]() -> const uint32_t(&)[4][VW] {
+          if constexpr (kVPre) return k.v[ks];
+          else if constexpr (kVChunk) return vc[ks];
+          else return vl;
+        }();
 #pragma unroll
         for (int j = 0; j < DPL; ++j) {
-          half4_t a = half4_t{vr[ks][0][j], vr[ks][1][j], vr[ks][2][j], vr[ks][3][j]};
+          const half4_t a = gather_col_f16<VW>(vb[0], vb[1], vb[2], vb[3], j);
           oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, bop, oacc[j], 0, 0, 0);
         }
       }
     } else {
 #pragma unroll 4
       for (int ks = 0; ks < 16; ++ks) {
-        const vrow_t a = load_vrow_buf<PT, DPL, vrow_t>(rv, voff_v, (c + 4 * ks) * D * (int)sizeof(PT));
+        const vrow_t a = load_vrow_buf<PT, DPL, vrow_t>(rv, voff_v, (cc + 4 * ks) * D * (int)sizeof(PT));
         float bop = 0.0f;
         if (r16 < GG) bop = pw[r16 * kChunk + 4 * ks + kq];
 #pragma unroll
@@ -522,6 +596,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     }
     wave_lds_sync();
+  };
+
+  for (; c < n_valid; c += 2 * STR) {
+    fetch(c + STR, kb);
+    process(c, ka);
+    if (c + STR >= n_valid) break;
+    fetch(c + 2 * STR, ka);
+    process(c + STR, kb);
   }
 
   // ---- merge the four waves through LDS (the table is no longer needed)
@@ -628,7 +710,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 }
 
 template <class S, int GG>
-__global__ __launch_bounds__(kThreads) void score_kernel(const AttnParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_kernel(const AttnParams p) {
   using Plan = LdsPlan<S, GG>;
   constexpr int HW = Plan::HW;
   __shared__ __align__(16) unsigned char smem[Plan::pst_off];
@@ -649,26 +731,43 @@ __global__ __launch_bounds__(kThreads) void score_kernel(const AttnParams p) {
   const __amdgpu_buffer_rsrc_t rn = make_rsrc(S::kNorm ? (const void*)(p.norms + rowb) : (const void*)p.codes,
                                               S::kNorm ? (int64_t)n_valid * 4 : 0);
 
-  prologue<S, GG>(p, u, qs, lv, tid, [] {});
+  // codes and norms one chunk (of this wave) ahead, in two alternating register sets (as in decode_kernel)
+  constexpr int STR = kWaves * kChunk;
+  uint32_t wa[S::NW], wb[S::NW];
+  float na = 1.0f, nb = 1.0f;
+  auto fetch = [&](int cc, uint32_t (&w)[S::NW], float& n) {
+    load_code_row_buf<S::BPK>(rc, lane * S::BPK, cc * S::BPK, w);
+    if constexpr (S::kNorm) n = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, 0));
+  };
+  // the unit's GG score rows through a buffer resource: 32-bit offsets, head row in the scalar offset,
+  // and stores at or past T_cap are dropped by the bounds check
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scores + ((size_t)u.b * p.Hq + u.h0) * p.T_cap,
+                                              (int64_t)GG * p.T_cap * 4);
+  auto score = [&](int cc, const uint32_t (&w)[S::NW], float n) {
+    float acc[GG];
+    lut_scores<S, GG>(smem, w, acc);
+    const int t = cc + lane;
+    const bool valid = t < n_valid;
+    // past the split: an offset beyond the resource (2^30 > GG*T_cap*4, which the host checks), so dropped
+    const int voff = t < n_stop ? (int)(t_begin + t) * 4 : 0x40000000;
+#pragma unroll
+    for (int g = 0; g < GG; ++g) {
+      const float sc = S::kNorm ? n * acc[g] : acc[g];
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, valid ? sc : -INFINITY), rs, voff,
+                                            g * p.T_cap * 4, 0);
+    }
+  };
+  int c = wid * kChunk;
+  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c, wa, na); });
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   lds_barrier();
 
-  for (int c = wid * kChunk; c < n_stop; c += kWaves * kChunk) {
-    uint32_t w[S::NW];
-    float nrm = 1.0f;
-    load_code_row_buf<S::BPK>(rc, lane * S::BPK, c * S::BPK, w);
-    if constexpr (S::kNorm) nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, c * 4, 0));
-    float acc[GG];
-    lut_scores<S, GG>(smem, w, acc);
-    const int t = c + lane;
-    if (t < n_stop) {
-      const bool valid = t < n_valid;
-#pragma unroll
-      for (int g = 0; g < GG; ++g) {
-        const float s = S::kNorm ? nrm * acc[g] : acc[g];
-        p.scores[((size_t)u.b * p.Hq + u.h0 + g) * p.T_cap + t_begin + t] = valid ? s : -INFINITY;
-      }
-    }
+  for (; c < n_stop; c += 2 * STR) {
+    fetch(c + STR, wb, nb);
+    score(c, wa, na);
+    if (c + STR >= n_stop) break;
+    fetch(c + 2 * STR, wa, na);
+    score(c + STR, wb, nb);
   }
 }
 

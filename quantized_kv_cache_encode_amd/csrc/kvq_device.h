@@ -17,6 +17,9 @@ template <> struct VecF<1> { typedef float type; };
 template <> struct VecF<2> { typedef float2 type; };
 template <> struct VecF<4> { typedef float4 type; };
 
+__device__ __forceinline__ void set_from(float* acc, float e) { acc[0] = e; }
+__device__ __forceinline__ void set_from(float* acc, float2 e) { acc[0] = e.x; acc[1] = e.y; }
+__device__ __forceinline__ void set_from(float* acc, float4 e) { acc[0] = e.x; acc[1] = e.y; acc[2] = e.z; acc[3] = e.w; }
 __device__ __forceinline__ void add_into(float* acc, float e) { acc[0] += e; }
 __device__ __forceinline__ void add_into(float* acc, float2 e) { acc[0] += e.x; acc[1] += e.y; }
 __device__ __forceinline__ void add_into(float* acc, float4 e) {
@@ -36,16 +39,42 @@ __device__ __forceinline__ void lds_barrier() {
 // between lanes of one wave through LDS).
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Value of x in another lane of the same row of 16, selected by a DPP control word.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppHalfMir = 0x141;  // row_half_mirror: lane i <- 7-i within 8
+constexpr int kDppMirror = 0x140;   // row_mirror: lane i <- 15-i within 16
+
+// Wave-wide reductions: within each row of 16 lanes through DPP moves, then across the four rows through
+// lanes 0, 16, 32, 48.  The result is the same in every lane.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  x = fmaxf(x, dpp_f<kDppSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppSwap2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMir>(x));
+  x = fmaxf(x, dpp_f<kDppMirror>(x));
+  const int xi = __builtin_bit_cast(int, x);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x += dpp_f<kDppSwap1>(x);
+  x += dpp_f<kDppSwap2>(x);
+  x += dpp_f<kDppHalfMir>(x);
+  x += dpp_f<kDppMirror>(x);
+  const int xi = __builtin_bit_cast(int, x);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(xi, 48));
+  return (a + b) + (c + d);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
