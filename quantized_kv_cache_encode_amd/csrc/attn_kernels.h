@@ -143,8 +143,8 @@ struct LdsPlan {
   static constexpr size_t lut_bytes = (size_t)GG * S::ROWS * S::COLS * 4;
   static constexpr size_t red_bytes = (size_t)kWaves * GG * (S::D + 2) * 4;
   static constexpr size_t region0 = ((lut_bytes > red_bytes ? lut_bytes : red_bytes) + 15) / 16 * 16;
-  static constexpr size_t consts_off = region0;                   // 16 levels, 8 sign words, flags
-  static constexpr size_t qs_off = consts_off + 128;              // GG * D floats
+  static constexpr size_t consts_off = region0;                   // 16 levels, flags, per-wave progress
+  static constexpr size_t qs_off = consts_off + 160;              // GG * D floats
   static constexpr size_t pst_off = qs_off + (size_t)GG * S::D * 4;
   static constexpr size_t pst_bytes(bool f16) { return (size_t)kWaves * GG * kChunk * (f16 ? 2 : 4); }
   static constexpr size_t total(bool f16) { return pst_off + pst_bytes(f16); }
@@ -452,6 +452,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   __shared__ __align__(16) unsigned char smem[Plan::total(VF16)];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
   int* s_flag = reinterpret_cast<int*>(smem + Plan::consts_off + 96);
+  volatile int* s_prog = reinterpret_cast<int*>(smem + Plan::consts_off + 128);  // [kWaves] chunks done
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
   PT* pst = reinterpret_cast<PT*>(smem + Plan::pst_off);
 
@@ -496,19 +497,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
     for (int s = 0; s < 4; ++s) load_vwords_f16<DPL>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT), vb[s]);
   };
-  auto fetch = [&](int cc, Chunk& k) {
+  auto fetch_codes = [&](int cc, Chunk& k) {
     load_code_row_buf<S::BPK>(rc, voff_code, cc * S::BPK, k.w);
     k.nrm = 1.0f;
     if constexpr (S::kNorm) k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, 0));
+  };
+  auto fetch_v = [&](int cc, Chunk& k) {
     if constexpr (kVPre) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) load_v(cc, ks, k.v[ks]);
     }
   };
+  auto fetch = [&](int cc, Chunk& k) {
+    fetch_codes(cc, k);
+    fetch_v(cc, k);
+  };
   int c = wid * kChunk;  // chunk start, relative to t_begin
   Chunk ka, kb;
-  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c, ka); });
+  // Only the first chunk's codes and norms are requested before the queries arrive (a smaller burst
+  // ahead of the query loads); its V follows once the table is built.
+  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch_codes(c, ka); });
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  fetch_v(c, ka);
+  if (lane == 0) s_prog[wid] = 0;
   lds_barrier();
 
   float m_run[GG], l_lane[GG];
@@ -521,6 +532,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
   for (int j = 0; j < DPL; ++j) oacc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
   PT* pw = pst + wid * GG * kChunk;
+  int done = 0;  // chunks this wave has processed
 
   // score one chunk (keys cc .. cc+63 of the split) and fold it into the softmax state and the output
   auto process = [&](int cc, const Chunk& k) {
@@ -596,6 +608,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     }
     wave_lds_sync();
+
+    // ---- keep the two waves that share a SIMD (wid and wid ^ kWaves/2) level: the instruction arbiter
+    // favours the older wave, which would otherwise finish well before its partner and leave the SIMD
+    // half occupied for the rest of the split.  A wave that is ahead drops its priority.
+    ++done;
+    if (lane == 0) s_prog[wid] = done;
+    const int other = __builtin_amdgcn_readfirstlane(s_prog[wid ^ (kWaves / 2)]);
+    if (done > other) __builtin_amdgcn_s_setprio(0);
+    else __builtin_amdgcn_s_setprio(1);
   };
 
   for (; c < n_valid; c += 2 * STR) {
@@ -610,7 +631,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   float l_w[GG];
 #pragma unroll
   for (int g = 0; g < GG; ++g) l_w[g] = wave_sum(l_lane[g]);
-  __syncthreads();
+  __builtin_amdgcn_s_setprio(0);
+  lds_barrier();  // every wave is done with the table, whose space now holds the per-wave partials
   float* red = reinterpret_cast<float*>(smem);            // [kWaves][GG][D]
   float* red_m = red + kWaves * GG * D;                    // [kWaves][GG]
   float* red_l = red_m + kWaves * GG;                      // [kWaves][GG]
@@ -626,7 +648,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       red_m[wid * GG + g] = m_run[g];
       red_l[wid * GG + g] = l_w[g];
     }
-  __syncthreads();
+  lds_barrier();
   for (int idx = tid; idx < GG * D; idx += kThreads) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
