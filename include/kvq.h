@@ -159,9 +159,12 @@ kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q,
  * count (n_splits = 0: the library's choice).  0 on invalid arguments. */
 size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv, int64_t T_cap, int n_splits);
 
-/* Fused decode attention from codes: scores, online softmax over t of
- * scale * s, and the AV product over v, in one pass over the cache split
- * along T across workgroups, followed by a log-sum-exp merge of the splits.
+/* Fused decode attention from codes (AXELRAM, Abstract: scores by table
+ * lookup on read, no inverse transform; shift-accumulate attention page,
+ * English abstract: decode attention fused with an online softmax): scores,
+ * online softmax over t of scale * s, and the AV product over v, in one pass
+ * over the cache split along T across workgroups, followed by a log-sum-exp
+ * merge of the splits.
  *   v:        device [B][Hkv][T_cap][d], dtype vdtype.
  *   scale:    softmax scale (1/sqrt(d) for standard attention).
  *   out:      device [B][Hq][d], dtype odtype, written.  A sequence of
@@ -175,12 +178,34 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
  *             Calls that share a workspace concurrently race.
  *   n_splits: 0 = library's choice; otherwise 1..T_cap/64 rounded up (the
  *             result is the same up to rounding for every n_splits).
- * Errors: as kvq_encode_keys, plus KVQ_ERR_WORKSPACE. */
+ * Errors: as kvq_encode_keys, plus KVQ_ERR_WORKSPACE, and KVQ_ERR_UNSUPPORTED
+ *   when T_cap * 4 * max(d, 32) >= 2^31 (the kernels address a cache split
+ *   with 32-bit offsets). */
 kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
                            const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
                            int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
                            void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
                            void* stream);
+
+/* One decode step in one launch: write path and read path together (AXELRAM,
+ * Abstract: transform on write, table lookup on read).  For every (b, kv
+ * head) the key new_keys[b][h] is encoded exactly as kvq_encode_keys does and
+ * stored at position len_b - 1 of codes and norms (len_b = seq_lens[b]
+ * clamped to T_cap, or T_cap when seq_lens is NULL; nothing is stored when
+ * len_b = 0), and attention over positions [0, len_b), the new key included,
+ * is computed exactly as kvq_decode_attn does.  The result equals
+ * kvq_encode_keys(write_pos = len - 1) followed by kvq_decode_attn, bit for
+ * bit.  The new token's value must already be in v at position len_b - 1.
+ *   new_keys: device [B][Hkv][d], dtype kdtype, 16-byte aligned.
+ *   codes, norms: the cache, read and written (rows len_b - 1).
+ *   Every other argument as kvq_decode_attn, including the workspace (same
+ *   size, from kvq_decode_attn_workspace).
+ * Errors: as kvq_decode_attn; KVQ_ERR_UNSUPPORTED for a PQ codebook. */
+kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, const void* new_keys,
+                                  kvq_dtype kdtype, const void* q, kvq_dtype qdtype, uint8_t* codes, float* norms,
+                                  const void* v, kvq_dtype vdtype, int B, int Hq, int Hkv, int64_t T_cap,
+                                  const int32_t* seq_lens, float scale, void* out, kvq_dtype odtype,
+                                  void* workspace, size_t ws_bytes, int n_splits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -304,11 +304,16 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
   return workspace_bytes(units, B, Hq, splits, cb->d);
 }
 
-kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
-                           const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
-                           int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
-                           void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of kvq_decode_attn and kvq_decode_attn_append (new_keys == nullptr: no append).
+kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t* signs, const void* new_keys,
+                         kvq_dtype kdtype, const void* q, kvq_dtype qdtype, const uint8_t* codes, const float* norms,
+                         const void* v, kvq_dtype vdtype, int B, int Hq, int Hkv, int64_t T_cap,
+                         const int32_t* seq_lens, float scale, void* out, kvq_dtype odtype, void* workspace,
+                         size_t ws_bytes, int n_splits, void* stream) {
   kvq::AttnParams p;
   ReadShape rs;
   kvq_status st = check_read(cb, signs, q, qdtype, codes, norms, B, Hq, Hkv, T_cap, &p, &rs);
@@ -318,6 +323,17 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
   if (!aligned16(v) || !aligned16(out)) return fail(KVQ_ERR_INVALID_ARG, "v or out not 16-byte aligned");
   if (n_splits < 0) return fail(KVQ_ERR_INVALID_ARG, "n_splits=%d", n_splits);
   if (!std::isfinite(scale)) return fail(KVQ_ERR_INVALID_ARG, "scale is not finite");
+  if (new_keys) {
+    if (cb->kind != KVQ_HADAMARD_LM)
+      return fail(KVQ_ERR_UNSUPPORTED, "the fused append supports the Hadamard/Lloyd-Max codec only");
+    if (!valid_dtype(kdtype)) return fail(KVQ_ERR_INVALID_ARG, "bad key dtype %d", (int)kdtype);
+    if (!aligned16(new_keys)) return fail(KVQ_ERR_INVALID_ARG, "new_keys not 16-byte aligned");
+    p.new_keys = new_keys;
+    p.new_f16 = kdtype == KVQ_F16;
+    p.app_codes = const_cast<uint8_t*>(codes);
+    p.app_norms = const_cast<float*>(norms);
+    for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
+  }
   p.seq_lens = seq_lens;
   p.v = v;
   p.out = out;
@@ -338,7 +354,30 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
   hipError_t e = cb->kind == KVQ_HADAMARD_LM
                      ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
                      : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
-  return from_hip(e, "kvq_decode_attn");
+  return from_hip(e, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                           const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
+                           int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
+                           void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
+                           void* stream) {
+  return decode_common("kvq_decode_attn", cb, signs, nullptr, KVQ_F32, q, qdtype, codes, norms, v, vdtype, B, Hq,
+                       Hkv, T_cap, seq_lens, scale, out, odtype, workspace, ws_bytes, n_splits, stream);
+}
+
+kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, const void* new_keys,
+                                  kvq_dtype kdtype, const void* q, kvq_dtype qdtype, uint8_t* codes, float* norms,
+                                  const void* v, kvq_dtype vdtype, int B, int Hq, int Hkv, int64_t T_cap,
+                                  const int32_t* seq_lens, float scale, void* out, kvq_dtype odtype,
+                                  void* workspace, size_t ws_bytes, int n_splits, void* stream) {
+  if (!new_keys) return fail(KVQ_ERR_INVALID_ARG, "new_keys is NULL");
+  return decode_common("kvq_decode_attn_append", cb, signs, new_keys, kdtype, q, qdtype, codes, norms, v, vdtype, B,
+                       Hq, Hkv, T_cap, seq_lens, scale, out, odtype, workspace, ws_bytes, n_splits, stream);
 }
 
 }  // extern "C"

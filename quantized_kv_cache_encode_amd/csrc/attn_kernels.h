@@ -36,6 +36,7 @@
 
 #include <type_traits>
 
+#include "encode_dev.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -65,6 +66,7 @@ struct HlmScorer {
   static constexpr int D = D_;
   static constexpr int ROWS = D;
   static constexpr int COLS = 1 << BITS;
+  static constexpr int CODE_BITS = BITS;
   static constexpr int BPK = D * BITS / 8;
   static constexpr int NW = (BPK + 3) / 4;
   static constexpr bool kRotate = true;
@@ -106,6 +108,7 @@ struct PqScorer {
   static constexpr int D = D_;
   static constexpr int ROWS = M;
   static constexpr int COLS = 256;
+  static constexpr int CODE_BITS = 8;
   static constexpr int BPK = M;
   static constexpr int NW = (BPK + 3) / 4;
   static constexpr int DS = D / M;
@@ -143,8 +146,12 @@ struct LdsPlan {
   static constexpr size_t lut_bytes = (size_t)GG * S::ROWS * S::COLS * 4;
   static constexpr size_t red_bytes = (size_t)kWaves * GG * (S::D + 2) * 4;
   static constexpr size_t region0 = ((lut_bytes > red_bytes ? lut_bytes : red_bytes) + 15) / 16 * 16;
-  static constexpr size_t consts_off = region0;                   // 16 levels, flags, per-wave progress
-  static constexpr size_t qs_off = consts_off + 160;              // GG * D floats
+  // consts: 16 levels (+0), merge flag (+96), per-wave progress (+128), appended key's codes (+160) and
+  // norm (+288)
+  static constexpr size_t consts_off = region0;
+  static constexpr size_t newcode_off = consts_off + 160;
+  static constexpr size_t newnorm_off = consts_off + 288;
+  static constexpr size_t qs_off = consts_off + 304;              // GG * D floats
   static constexpr size_t pst_off = qs_off + (size_t)GG * S::D * 4;
   static constexpr size_t pst_bytes(bool f16) { return (size_t)kWaves * GG * kChunk * (f16 ? 2 : 4); }
   static constexpr size_t total(bool f16) { return pst_off + pst_bytes(f16); }
@@ -453,6 +460,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
   int* s_flag = reinterpret_cast<int*>(smem + Plan::consts_off + 96);
   volatile int* s_prog = reinterpret_cast<int*>(smem + Plan::consts_off + 128);  // [kWaves] chunks done
+  uint32_t* s_newc = reinterpret_cast<uint32_t*>(smem + Plan::newcode_off);
+  float* s_newn = reinterpret_cast<float*>(smem + Plan::newnorm_off);
+  static_assert(S::NW * 4 <= 128, "appended key's codes fit their LDS slot");
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
   PT* pst = reinterpret_cast<PT*>(smem + Plan::pst_off);
 
@@ -514,9 +524,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   };
   int c = wid * kChunk;  // chunk start, relative to t_begin
   Chunk ka, kb;
+
+  // Fused append (Hadamard/Lloyd-Max codec): the workgroup whose split holds the sequence's last position
+  // encodes the new key itself -- wave 1, D/8 lanes, with the arithmetic of the encode kernel -- keeps its
+  // codes and norm in LDS for its own scores, and (head group 0 only) writes them to the cache.  Every
+  // wave issues the key load; it reads zeros except in the encoding lanes, so it needs no branch.
+  constexpr int LPK = D / 8;
+  const bool app = S::kRotate && p.new_keys != nullptr && n_valid > 0 && u.len <= t_begin + p.split_len;
+  const int rel = n_valid - 1;  // the new key's position within the split, when app
+  const bool enc_lanes = app && wid == 1 && lane < LPK;
+  const int64_t new_row = (int64_t)u.b * p.Hkv + u.kvh;
+  const int kesz = p.new_f16 ? 2 : 4;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_rsrc(app ? (const void*)(reinterpret_cast<const char*>(p.new_keys) + new_row * D * kesz) : p.codes,
+                app && wid == 1 ? D * kesz : 0);
+  uint32_t kraw[8];
+
   // Only the first chunk's codes and norms are requested before the queries arrive (a smaller burst
   // ahead of the query loads); its V follows once the table is built.
-  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch_codes(c, ka); });
+  prologue<S, GG>(p, u, qs, lv, tid, [&] {
+    fetch_codes(c, ka);
+    const int ko = lane * 8 * kesz;
+    const auto r0 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
+    const auto r1 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kraw[j] = r0[j];
+      kraw[4 + j] = r1[j];
+    }
+  });
+  if constexpr (S::kRotate) {
+    if (enc_lanes) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        x[j] = p.new_f16 ? h2f((uint16_t)(kraw[j / 2] >> (16 * (j % 2)))) : __builtin_bit_cast(float, kraw[j]);
+      float nrm;
+      const uint32_t packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
+      store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
+      if (lane == 0) *s_newn = nrm;
+      if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)
+        const int64_t row = new_row * p.T_cap + (u.len - 1);
+        store_code_bits<S::CODE_BITS>(p.app_codes + row * S::BPK, lane, packed);
+        if (lane == 0) p.app_norms[row] = nrm;
+      }
+    }
+  }
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   fetch_v(c, ka);
   if (lane == 0) s_prog[wid] = 0;
@@ -535,7 +588,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   int done = 0;  // chunks this wave has processed
 
   // score one chunk (keys cc .. cc+63 of the split) and fold it into the softmax state and the output
-  auto process = [&](int cc, const Chunk& k) {
+  auto process = [&](int cc, Chunk& k) {
+    if (app && cc <= rel && rel < cc + kChunk) {  // the appended key: codes and norm from LDS
+      if (lane == rel - cc) {
+#pragma unroll
+        for (int kk = 0; kk < S::NW; ++kk) k.w[kk] = s_newc[kk];
+        k.nrm = *s_newn;
+      }
+    }
     uint32_t vc[kVChunk ? 4 : 1][4][VW];  // d = 128: this chunk's V, requested before the gathers
     if constexpr (kVChunk) {
 #pragma unroll

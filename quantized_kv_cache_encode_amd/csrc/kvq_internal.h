@@ -35,6 +35,13 @@ struct AttnParams {
   float zscale;              // softmax scale * log2(e)
   float levels[16];
   uint32_t signs[8];         // bit i set <=> coordinate i is negated
+  // fused append (Hadamard/Lloyd-Max only): one new key per (b, kv head) stored at position len-1 and
+  // attended in the same call; new_keys == nullptr disables it
+  const void* new_keys;      // [B][Hkv][D] fp16 or fp32
+  uint8_t* app_codes;        // the code cache, written at the new rows (same buffer as codes)
+  float* app_norms;          // the norm cache, written at the new rows (same buffer as norms)
+  int new_f16;
+  float thresholds[15];
 };
 
 struct EncodeParams {

@@ -75,12 +75,14 @@ _lib.kvq_decode_attn_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
 _lib.kvq_decode_attn_workspace.restype = _sz
 _lib.kvq_decode_attn.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P, _f32,
                                  _P, _i32, _P, _sz, _i32, _P]
+_lib.kvq_decode_attn_append.argtypes = [_CB, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P,
+                                        _f32, _P, _i32, _P, _sz, _i32, _P]
 for _f in ("kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
-           "kvq_decode_attn"):
+           "kvq_decode_attn", "kvq_decode_attn_append"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq",
-           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn")
+           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append")
 
 
 def _check(status: int):
@@ -215,4 +217,30 @@ def kvq_decode_attn(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tenso
                                 _dev(norms, "norms", torch.float32, optional=True), _dev(v, "v"), _dt(v), B, Hq, Hkv,
                                 T_cap, _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
                                 _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
+    return out
+
+
+def kvq_decode_attn_append(cb: kvq_codebook, signs, new_keys: torch.Tensor, q: torch.Tensor, codes: torch.Tensor,
+                           norms: torch.Tensor, v: torch.Tensor, scale: float | None = None, seq_lens=None, out=None,
+                           out_dtype=None, workspace=None, n_splits: int = 0, stream=None) -> torch.Tensor:
+    """Encode new_keys [B][Hkv][d] at position len-1 of the cache, then attention as kvq_decode_attn."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = codes.shape
+    if tuple(new_keys.shape) != (B, Hkv, d):
+        raise ValueError("new_keys must have shape (%d, %d, %d)" % (B, Hkv, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype or v.dtype, device=q.device)
+    need = kvq_decode_attn_workspace(cb, B, Hq, Hkv, T_cap, n_splits)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
+    ws_ptr = _dev(workspace, "workspace", optional=True)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    s_np, s_ptr = _signs_host(signs, d)
+    _check(_lib.kvq_decode_attn_append(ctypes.byref(cb), s_ptr, _dev(new_keys, "new_keys"), _dt(new_keys), _dev(q, "q"),
+                                       _dt(q), _dev(codes, "codes", torch.uint8),
+                                       _dev(norms, "norms", torch.float32), _dev(v, "v"), _dt(v), B, Hq, Hkv, T_cap,
+                                       _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
+                                       _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
     return out

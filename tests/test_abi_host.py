@@ -165,3 +165,32 @@ def test_pq_codebook_validation(K):
         K._check(K._lib.kvq_codebook_pq(64, 8, 300, 12, ctypes.c_void_p(FAKE), ctypes.byref(K.kvq_codebook())))
     with pytest.raises(K.KvqError):
         K.kvq_build_codebook_pq(np.zeros((1, 10, 8), np.float32), 2, 4, 3, np.full((1, 2, 4), 11))
+
+
+def test_append_validation(K):
+    import ctypes
+    P = ctypes.c_void_p
+    cb = K.kvq_build_codebook(64, 4)
+    s = np.ones(64, dtype=np.int8)
+    lib = K._lib
+
+    def call(cbx, new_keys=FAKE, kdt=1):
+        return lib.kvq_decode_attn_append(ctypes.byref(cbx), s.ctypes.data_as(P), None if new_keys is None else P(new_keys),
+                                          kdt, P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), 1, 1, 4, 2, 64, None, 0.125,
+                                          P(FAKE), 1, None, 0, 0, None)
+    assert call(cb, new_keys=None) == K.KVQ_ERR_INVALID_ARG
+    assert "new_keys" in K.kvq_last_error()
+    assert call(cb, new_keys=FAKE + 4) == K.KVQ_ERR_INVALID_ARG
+    assert call(cb, kdt=3) == K.KVQ_ERR_INVALID_ARG
+    pq = K.kvq_codebook()
+    K._check(lib.kvq_codebook_pq(64, 8, 256, 2, P(FAKE), ctypes.byref(pq)))
+    assert call(pq) == K.KVQ_ERR_UNSUPPORTED
+    assert "Hadamard" in K.kvq_last_error()
+
+
+def test_offset_limit(K):
+    """T_cap beyond the kernels' 32-bit offsets is rejected before any launch."""
+    cb = K.kvq_build_codebook(256, 4)
+    s = np.ones(256, dtype=np.int8)
+    assert _call_decode(K, cb, s, T_cap=(1 << 31) // (4 * 256)) == K.KVQ_ERR_UNSUPPORTED
+    assert "32-bit" in K.kvq_last_error()
