@@ -107,6 +107,154 @@ def cpu_baseline(shape, signs, q, min_seconds=5.0):
                       "keys + decode attention, one thread, %.1f s" % (shape.B, shape.Hq, shape.T, passes, elapsed)}
 
 
+def run_suite(K, torch, reps=5, calls=30):
+    """Every configuration of the method on one GPU: read path (fused decode, scores alone), write path
+    (encode), and the PQ variant.  Inputs are drawn on the GPU from a seeded generator with the workloads'
+    shapes and distributions (normal keys and values; per-(kv head, channel) LogNormal(0,1) scales for the
+    Llama-8B-like shapes, per-token LogNormal(0,0.5) key scales for the long-context one); at least four
+    distinct caches rotate so every call streams from HBM.  Each figure is the median over `reps` graph
+    replays of `calls` calls.  Prints one table row per (workload, operation)."""
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2024)
+    rows = []
+
+    def rnd(*shape):
+        return torch.randn(shape, device=dev, dtype=torch.float32, generator=gen)
+
+    def draw_keys(sh, T):
+        k = rnd(sh.B, sh.Hkv, T, sh.d)
+        if sh.key_scale == "channel_lognormal":
+            k *= torch.exp(rnd(1, sh.Hkv, 1, sh.d))
+        elif sh.key_scale == "token_lognormal":
+            k *= torch.exp(0.5 * rnd(sh.B, sh.Hkv, T, 1))
+        return k.half()
+
+    def draw_values(sh, T):
+        v = rnd(sh.B, sh.Hkv, T, sh.d)
+        if sh.v_scale == "channel_lognormal":
+            v *= torch.exp(rnd(1, sh.Hkv, 1, sh.d))
+        return v.half()
+
+    def timed(fn, n_rot):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(max(n_rot, 3)):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / calls)
+        ts.sort()
+        return ts[len(ts) // 2] * 1e-3  # seconds per call
+
+    def row(name, op, sec, nbytes, keys_scored, cached):
+        rows.append((name, op, sec * 1e6, nbytes / sec / 1e9, 100 * nbytes / sec / 1e9 / HBM_PEAK_GBS,
+                     keys_scored / sec if keys_scored else 0.0, cached / sec))
+        eprint("%-22s %-10s %10.2f us %9.1f GB/s %6.1f%%  %10.3g keys-scored/s %10.3g cached-keys/s" % rows[-1])
+
+    hlm = [("llama8b", W.LLAMA8B), ("longctx", W.LONGCTX)] + [(s.name, s) for s in W.SWEEP]
+    for name, sh in hlm:
+        B, Hq, Hkv, d, T, b = sh.B, sh.Hq, sh.Hkv, sh.d, sh.T, sh.b
+        cb = K.kvq_build_codebook(d, b)
+        bpk = cb.bytes_per_key
+        signs = W.signs(sh)
+        per_cache = B * Hkv * T * (bpk + 4 + 2 * d)
+        n_rot = max(4, int(math.ceil(1.2e9 / per_cache)))  # >= 4 caches and >= 1.2 GB in rotation
+        caches = []
+        keys = None
+        for r in range(n_rot):
+            if r == 0:
+                keys = draw_keys(sh, T)
+                codes = torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev)
+                norms = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                K.kvq_encode_keys(cb, signs, keys, codes, norms)
+                caches.append((codes, norms, draw_values(sh, T)))
+            else:
+                c0, n0, v0 = caches[0]
+                caches.append((c0.clone(), n0.clone(), v0.clone()))
+        q = rnd(B, Hq, d).half()
+        out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+        ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, 0), 16), dtype=torch.uint8, device=dev)
+        nk = draw_keys(sh, 1)[:, :, 0, :].contiguous()
+
+        def dec(i):
+            c, n, v = caches[i % n_rot]
+            K.kvq_decode_attn(cb, signs, q, c, n, v, out=out, workspace=ws)
+
+        def app(i):
+            c, n, v = caches[i % n_rot]
+            K.kvq_decode_attn_append(cb, signs, nk, q, c, n, v, out=out, workspace=ws)
+
+        scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+
+        def score(i):
+            c, n, _ = caches[i % n_rot]
+            K.kvq_score(cb, signs, q, c, n, scores=scores)
+
+        rd = algorithmic_bytes(sh, bpk)
+        row(name, "decode", timed(dec, n_rot), rd, B * Hq * T, B * Hkv * T)
+        row(name, "append+dec", timed(app, n_rot), algorithmic_bytes(sh, bpk, append=True), B * Hq * T, B * Hkv * T)
+        row(name, "score", timed(score, n_rot), B * Hkv * T * (bpk + 4) + B * Hq * T * 4, B * Hq * T, B * Hkv * T)
+
+        def enc(i):
+            c, n, _ = caches[i % n_rot]
+            K.kvq_encode_keys(cb, signs, keys, c, n)
+
+        row(name, "encode", timed(enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
+        del caches, keys, scores
+        torch.cuda.empty_cache()
+
+    # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes
+    sh = W.PQ_GPT2
+    B, H, d, T, m, Kc = sh.B, sh.Hq, sh.d, sh.T, sh.m, sh.K
+    cent = rnd(H, m, Kc, d // m)
+    cb = K.kvq_codebook_pq(d, m, Kc, H, cent)
+    n_rot = 8
+    keys = rnd(B, H, T, d).half()
+    codes0 = torch.empty((B, H, T, m), dtype=torch.uint8, device=dev)
+    K.kvq_encode_keys(cb, None, keys, codes0)
+    vals = rnd(B, H, T, d).half()
+    caches = [(codes0, vals)] + [(codes0.clone(), vals.clone()) for _ in range(n_rot - 1)]
+    q = rnd(B, H, d).half()
+    out = torch.empty((B, H, d), dtype=torch.float16, device=dev)
+    ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, H, H, T, 0), 16), dtype=torch.uint8, device=dev)
+    scores = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+
+    def pq_dec(i):
+        c, v = caches[i % n_rot]
+        K.kvq_decode_attn(cb, None, q, c, None, v, out=out, workspace=ws)
+
+    def pq_score(i):
+        c, _ = caches[i % n_rot]
+        K.kvq_score(cb, None, q, c, None, scores=scores)
+
+    def pq_enc(i):
+        c, _ = caches[i % n_rot]
+        K.kvq_encode_keys(cb, None, keys, c)
+
+    nkeys = B * H * T
+    row("pq_gpt2", "decode", timed(pq_dec, n_rot), nkeys * (m + 2 * d) + B * H * d * 2, nkeys, nkeys)
+    row("pq_gpt2", "score", timed(pq_score, n_rot), nkeys * (m + 4), nkeys, nkeys)
+    row("pq_gpt2", "encode", timed(pq_enc, n_rot), nkeys * (2 * d + m), 0, nkeys)
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +266,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=5.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
+    ap.add_argument("--suite", action="store_true",
+                    help="instead of the headline step, time every workload and operation (table on stderr)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -136,6 +286,9 @@ def main(argv=None):
     import quantized_kv_cache_encode_amd.kvq as K
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if a.suite:
+        run_suite(K, torch)
+        return 0
     dev = torch.device("cuda:0")
     shape = W.LONGCTX
     B, Hq, Hkv, d, T, b = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T, shape.b
