@@ -265,6 +265,12 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
     st = pack_signs(signs, cb->d, p.signs);
     if (st != KVQ_OK) return st;
     for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
+    if (!kvq::choose_encode_cells(cb->thresholds, (1 << cb->b) - 1, &p.n_cells, &p.cell_inv, &p.cell_shift))
+      return fail(KVQ_ERR_UNSUPPORTED, "no cell grid separates the codebook's thresholds");
+    if (T_new > 0 && (int64_t)B * Hkv * T_new >= ((int64_t)1 << 31))
+      return fail(KVQ_ERR_UNSUPPORTED, "B*Hkv*T_new must stay below 2^31");
+    if (T_new > 0) kvq::fast_div_magic((uint32_t)T_new, &p.tnew_magic, &p.tnew_shift);
+    kvq::fast_div_magic((uint32_t)Hkv, &p.hkv_magic, &p.hkv_shift);
     if (T_new == 0) return ok();
     return from_hip(kvq::launch_hlm_encode(cb->d, cb->b, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
   }

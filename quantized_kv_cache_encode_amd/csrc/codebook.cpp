@@ -5,6 +5,7 @@
 // the orthogonal transform has made every coordinate N(0,1/d)) and Lloyd
 // k-means for product-quantization codebooks ("LOOKAT" summary page, AI
 // Summary: codebook learning per subspace).
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -94,6 +95,41 @@ void kmeans_lloyd(const float* train, int64_t n, int dim, int stride, int K, int
       if (members[c] > 0)
         for (int k = 0; k < dim; ++k) cent[c * dim + k] = acc[(size_t)c * dim + k] / (double)members[c];
   }
+}
+
+// Grid of equal cells over y in [-1, 1] for the encode kernel's threshold search: code(y) = (thresholds
+// in cells below y's cell) + (y >= the threshold inside y's cell, if any).  That is exact as long as no
+// cell holds two thresholds and no threshold lies within the rounding of y's cell index of a cell
+// boundary; the grid is chosen so that every threshold sits in [5%, 95%] of its cell, computed with the
+// same fp32 fused multiply-add the kernel uses.
+bool choose_encode_cells(const float* t, int n, int* n_cells, float* cell_inv, float* cell_shift) {
+  double min_gap = 1.0;
+  for (int j = 0; j + 1 < n; ++j) min_gap = std::min(min_gap, (double)t[j + 1] - (double)t[j]);
+  double w = std::max(min_gap / 3.0, 2.0005 / (kEncodeMaxCells - 4));
+  for (int iter = 0; iter < 400; ++iter, w *= 0.997) {
+    const float inv = (float)(1.0 / w);
+    const int off = (int)std::ceil(1.0001 * (double)inv) + 1;
+    const int cells = 2 * off + 1;
+    if (cells > kEncodeMaxCells) return false;
+    for (int k = 0; k < 8; ++k) {
+      const float shift = (float)off + 0.5f + 0.0625f * (float)k;
+      bool good = true;
+      double prev_cell = -1e30;
+      for (int j = 0; j < n && good; ++j) {
+        const float v = std::fmaf(t[j], inv, shift);
+        const double fr = (double)v - std::floor((double)v);
+        if (fr < 0.05 || fr > 0.95 || std::floor((double)v) == prev_cell) good = false;
+        prev_cell = std::floor((double)v);
+      }
+      if (good) {
+        *n_cells = cells;
+        *cell_inv = inv;
+        *cell_shift = shift;
+        return true;
+      }
+    }
+  }
+  return false;
 }
 
 }  // namespace kvq

@@ -7,39 +7,69 @@
 // code_i = #{ j : t_j <= y_i } for the Lloyd-Max thresholds t of N(0, 1/d).
 #pragma once
 
+#include <type_traits>
+
 #include "kvq_device.h"
 
 namespace kvq {
 
-// One key is held by LPK = D/8 consecutive lanes (a power of two), 8 coordinates per lane: lane lk holds
-// coordinates 8*lk .. 8*lk+7 in x.  All LPK lanes must call this together.  Returns the lane's 8*BITS code
-// bits (coordinate 8*lk+j at bits [BITS*j, BITS*j+BITS)) and sets nrm = ||k|| in every lane of the key.
-// `signs` is the bit mask of D (bit i set: coordinate i negated), `thresholds` the L-1 ascending cell
-// boundaries of the codebook.
-template <int D, int BITS>
-__device__ __forceinline__ uint32_t encode_key_lane(float (&x)[8], int lk, const uint32_t* signs,
-                                                    const float* thresholds, float& nrm) {
-  constexpr int LPK = D / 8;
-  constexpr int L = 1 << BITS;
-  float ss = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) ss += x[j] * x[j];
-#pragma unroll
-  for (int o = 1; o < LPK; o <<= 1) ss += __shfl_xor(ss, o, 64);
+// x from the lane lk ^ DL of the same key (lanes of a key are consecutive, start at a multiple of their
+// count and stay within one half of the wave).  ds_swizzle in bit-mask mode (and 0x1f, or 0, xor DL)
+// permutes within each group of 32 lanes through the LDS crossbar without touching LDS memory, which keeps
+// the permutation off the vector ALU that the rest of the encode keeps busy.
+template <int DL>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(DL >= 1 && DL <= 16, "lane distance within 32 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (DL << 10) | 0x1f));
+}
 
-  // sign pattern D for coordinates lk*8 .. lk*8+7
+// Sum of v over the LPK lanes of the key (the same value in all of them).
+template <int LPK>
+__device__ __forceinline__ float key_lanes_sum(float v) {
+  if constexpr (LPK >= 2) v += xor_lane<1>(v);
+  if constexpr (LPK >= 4) v += xor_lane<2>(v);
+  if constexpr (LPK >= 8) v += xor_lane<4>(v);
+  if constexpr (LPK >= 16) v += xor_lane<8>(v);
+  if constexpr (LPK >= 32) v += xor_lane<16>(v);
+  return v;
+}
+
+// Sign of coordinate 8*lk + j under the pattern D (bit i of `signs` set: coordinate i negated), as +-1.
+template <int D>
+__device__ __forceinline__ void lane_signs(const uint32_t* signs, int lk, float (&sg)[8]) {
   uint32_t word = 0;
 #pragma unroll
   for (int k = 0; k < (D + 31) / 32; ++k)
     if (((lk * 8) >> 5) == k) word = signs[k];
   const uint32_t sb = (word >> ((lk * 8) & 31)) & 0xffu;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if ((sb >> j) & 1u) x[j] = -x[j];
+  for (int j = 0; j < 8; ++j) sg[j] = ((sb >> j) & 1u) ? -1.0f : 1.0f;
+}
 
-  // in-register butterflies (distances 1, 2, 4)
+// One key is held by LPK = D/8 consecutive lanes (a power of two), 8 coordinates per lane: lane lk holds
+// coordinates 8*lk .. 8*lk+7 in x.  All LPK lanes must run this together.  On return x holds those
+// coordinates of H' D k, where H' is the unnormalised Sylvester Walsh-Hadamard matrix, and the result is
+// ||k|| (the same in every lane of the key).  sg are the lane's signs from lane_signs.
+template <int D>
+__device__ __forceinline__ float rotate_key_lane(float (&x)[8], int lk, const float (&sg)[8]) {
+  constexpr int LPK = D / 8;
+  // explicit fused multiply-adds: the sum is the same wherever this is inlined (a plain x*x + ss would
+  // leave the compiler free to fuse differently in different callers)
+  float ss = x[0] * x[0];
 #pragma unroll
-  for (int h = 1; h < 8; h <<= 1)
+  for (int j = 1; j < 8; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
+  ss = key_lanes_sum<LPK>(ss);
+  // signs folded into the first butterflies: (s0 a + s1 c, s0 a - s1 c), each product exact
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float c = x[i + 1] * sg[i + 1];
+    const float a = x[i];
+    x[i] = __builtin_fmaf(a, sg[i], c);
+    x[i + 1] = __builtin_fmaf(a, sg[i], -c);
+  }
+  // remaining in-register butterflies (coordinate distances 2, 4)
+#pragma unroll
+  for (int h = 2; h < 8; h <<= 1)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if ((i & h) == 0) {
@@ -47,29 +77,56 @@ __device__ __forceinline__ uint32_t encode_key_lane(float (&x)[8], int lk, const
         x[i] = a + c;
         x[i + h] = a - c;
       }
-  // cross-lane butterflies (distances 8, 16, ... = lane distances 1, 2, ...)
+  // cross-lane butterflies (coordinate distances 8, 16, ... = lane distances 1, 2, ...): the lower lane
+  // of a pair keeps x + partner, the upper one partner - x, both as one fused multiply-add with +-1
+  auto stage = [&](auto dl_tag) {
+    constexpr int DL = decltype(dl_tag)::value;
+    const float s = (lk & DL) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int dl = 1; dl < LPK; dl <<= 1) {
-    const bool upper = (lk & dl) != 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float o = __shfl_xor(x[j], dl, 64);
-      x[j] = upper ? (o - x[j]) : (x[j] + o);
-    }
-  }
+    for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(x[j], s, xor_lane<DL>(x[j]));
+  };
+  if constexpr (LPK >= 2) stage(std::integral_constant<int, 1>{});
+  if constexpr (LPK >= 4) stage(std::integral_constant<int, 2>{});
+  if constexpr (LPK >= 8) stage(std::integral_constant<int, 4>{});
+  if constexpr (LPK >= 16) stage(std::integral_constant<int, 8>{});
+  if constexpr (LPK >= 32) stage(std::integral_constant<int, 16>{});
+  return __builtin_sqrtf(ss);
+}
 
-  nrm = __builtin_sqrtf(ss);
-  const float inv = nrm > 0.0f ? 1.0f / (nrm * __builtin_sqrtf((float)D)) : 0.0f;
+// 1 / (||k|| sqrt(d)): scales H' D k to the rotated unit vector y; 0 for a zero key.
+template <int D>
+__device__ __forceinline__ float unit_scale(float nrm) {
+  return nrm > 0.0f ? 1.0f / (nrm * __builtin_sqrtf((float)D)) : 0.0f;
+}
+
+// code = #{ j : t_j <= y } by comparing with every threshold.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_by_count(float y, const float* thresholds) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int t = 0; t < (1 << BITS) - 1; ++t) c += (y >= thresholds[t]) ? 1u : 0u;
+  return c;
+}
+
+// The lane's 8*BITS code bits: coordinate 8*lk+j at bits [BITS*j, BITS*j+BITS), y_j = x_j * inv.
+template <int BITS, class Q>
+__device__ __forceinline__ uint32_t pack_lane_codes(const float (&x)[8], float inv, Q&& code_of) {
   uint32_t packed = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float y = x[j] * inv;
-    uint32_t c = 0;
-#pragma unroll
-    for (int t = 0; t < L - 1; ++t) c += (y >= thresholds[t]) ? 1u : 0u;
-    packed |= c << (BITS * j);
-  }
+  for (int j = 0; j < 8; ++j) packed |= code_of(x[j] * inv) << (BITS * j);
   return packed;
+}
+
+// Encode of one key with the per-threshold comparison (used where a single key is encoded).  Same lane
+// layout and arithmetic as the encode kernel, whose table-driven cell search returns the same count.
+template <int D, int BITS>
+__device__ __forceinline__ uint32_t encode_key_lane(float (&x)[8], int lk, const uint32_t* signs,
+                                                    const float* thresholds, float& nrm) {
+  float sg[8];
+  lane_signs<D>(signs, lk, sg);
+  nrm = rotate_key_lane<D>(x, lk, sg);
+  const float inv = unit_scale<D>(nrm);
+  return pack_lane_codes<BITS>(x, inv, [&](float y) { return code_by_count<BITS>(y, thresholds); });
 }
 
 // Loads the 8 coordinates 8*lk .. 8*lk+7 of the key at `key` (fp16 or fp32, 16-byte aligned rows).

@@ -42,7 +42,7 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // Value of x in another lane of the same row of 16, selected by a DPP control word.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
 }
 constexpr int kDppSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kDppSwap2 = 0x4E;     // quad_perm [2,3,0,1]

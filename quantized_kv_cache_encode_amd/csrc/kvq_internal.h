@@ -55,7 +55,26 @@ struct EncodeParams {
   int pq_K;
   float thresholds[15];
   uint32_t signs[8];
+  // cell search of the Hadamard/Lloyd-Max encode: y (|y| <= 1) falls in cell floor(y * cell_inv +
+  // cell_shift) of n_cells; every threshold sits at least 5% of a cell away from a cell boundary and no
+  // cell holds two (choose_encode_cells)
+  int n_cells;
+  float cell_inv, cell_shift;
+  int64_t key_begin, key_end;  // the keys [key_begin, key_end) of [B*Hkv*T_new] this launch encodes
+  uint32_t tnew_magic, hkv_magic;  // n / T_new and n / Hkv for n < 2^31: (umulhi(n, magic) + n) >> shift
+  int tnew_shift, hkv_shift;
 };
+
+// Magic number and shift for division by d >= 1 of any n < 2^31 (round-up method).
+inline void fast_div_magic(uint32_t d, uint32_t* magic, int* shift) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  *shift = l;
+  *magic = (uint32_t)((((1ull << 32) * ((1ull << l) - d)) / d) + 1);
+  if (d == 1) *magic = 0;
+}
+
+constexpr int kEncodeMaxCells = 1024;
 
 // Kernel launchers.  Each returns hipSuccess or the launch error; an
 // unsupported template combination returns hipErrorNotSupported without
@@ -68,6 +87,9 @@ hipError_t launch_pq_decode(int D, int M, int heads_per_wg, bool v_f16, const At
 hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_hlm_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
 hipError_t launch_pq_encode(int D, int M, bool k_f16, const EncodeParams& p, hipStream_t s);
+
+// Cell grid for the encode's threshold search (codebook.cpp); false if none fits kEncodeMaxCells.
+bool choose_encode_cells(const float* thresholds, int n_thresholds, int* n_cells, float* cell_inv, float* cell_shift);
 
 // Host codebook construction (codebook.cpp).
 void lloyd_max_gaussian(int b, double* levels, double* thresholds);
