@@ -42,69 +42,55 @@ hipError_t launch_pq_score(int D, int M, int gg, const AttnParams& p, dim3 grid,
   }
 }
 
-// One workgroup = 256 keys of one (batch, kv head); that head's centroids
-// [M][K][D/M] are staged in LDS and every lane scans them for its key
-// (all lanes read the same centroid at once: an LDS broadcast).  Squared
-// distances in fp32; ties keep the lowest index.
+// One workgroup = 256 keys of one (batch, kv head) and one subspace s: that subspace's centroids [K][D/M]
+// are staged in LDS and every lane scans them for its key's sub-vector (all lanes read the same centroid at
+// once: an LDS broadcast).  Squared distances sum (x_k - c_k)^2 in fp32 in coordinate order; ties keep the
+// lowest index.  Parallel over (key, subspace), so even a short cache fills the chip.
 template <int D, int M, bool KF16>
 __global__ __launch_bounds__(256) void pq_encode_kernel(const EncodeParams p) {
   constexpr int DS = D / M;
   extern __shared__ __align__(16) float cent_s[];
   const int K = p.pq_K;
   const int bh = blockIdx.y;
+  const int s = blockIdx.z;
   const int h = bh % p.Hkv, b = bh / p.Hkv;
-  const float* cg = p.pq_cent + (size_t)h * M * K * DS;
-  for (int x = threadIdx.x; x < M * K * DS; x += 256) cent_s[x] = cg[x];
+  const float* cg = p.pq_cent + ((size_t)h * M + s) * K * DS;
+  for (int x = threadIdx.x; x < K * DS; x += 256) cent_s[x] = cg[x];
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= p.T_new) return;
   const int64_t pos = (p.write_pos ? (int64_t)p.write_pos[b] : p.t0) + t;
   if (pos < 0 || pos >= p.T_cap) return;
-  const size_t src = ((size_t)bh * p.T_new + t) * D;
-  uint32_t words[M / 4];
+  const size_t src = ((size_t)bh * p.T_new + t) * D + (size_t)s * DS;
+  float x[DS];
 #pragma unroll
-  for (int k = 0; k < M / 4; ++k) words[k] = 0;
+  for (int k = 0; k < DS; ++k)
+    x[k] = KF16 ? (float)reinterpret_cast<const _Float16*>(p.keys)[src + k] : reinterpret_cast<const float*>(p.keys)[src + k];
+  int best = 0;
+  float bd = INFINITY;
+#pragma unroll 4
+  for (int c = 0; c < K; ++c) {
+    const float* cc = cent_s + (size_t)c * DS;
+    float dist = 0.0f;
 #pragma unroll
-  for (int s = 0; s < M; ++s) {
-    float x[DS];
-#pragma unroll
-    for (int k = 0; k < DS; ++k)
-      x[k] = KF16 ? (float)reinterpret_cast<const _Float16*>(p.keys)[src + s * DS + k]
-                  : reinterpret_cast<const float*>(p.keys)[src + s * DS + k];
-    int best = 0;
-    float bd = INFINITY;
-    for (int c = 0; c < K; ++c) {
-      const float* cc = cent_s + ((size_t)s * K + c) * DS;
-      float dist = 0.0f;
-#pragma unroll
-      for (int k = 0; k < DS; ++k) {
-        const float e = x[k] - cc[k];
-        dist += e * e;
-      }
-      if (dist < bd) {
-        bd = dist;
-        best = c;
-      }
+    for (int k = 0; k < DS; ++k) {
+      const float e = x[k] - cc[k];
+      dist = __builtin_fmaf(e, e, dist);
     }
-    words[s / 4] |= (uint32_t)best << (8 * (s % 4));
+    if (dist < bd) {
+      bd = dist;
+      best = c;
+    }
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(p.codes + ((size_t)bh * p.T_cap + pos) * M);
-#pragma unroll
-  for (int k = 0; k < M / 4; ++k) dst[k] = words[k];
+  p.codes[((size_t)bh * p.T_cap + pos) * M + s] = (uint8_t)best;
 }
 
 template <int D, int M, bool KF16>
 static hipError_t pq_encode_launch(const EncodeParams& p, hipStream_t s) {
-  const size_t lds = (size_t)D * p.pq_K * 4;
-  if (lds > 160 * 1024) return hipErrorNotSupported;
-  auto kern = pq_encode_kernel<D, M, KF16>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid((unsigned)((p.T_new + 255) / 256), (unsigned)(p.B * p.Hkv));
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+  const size_t lds = (size_t)(D / M) * p.pq_K * 4;
+  if (lds > 64 * 1024) return hipErrorNotSupported;
+  dim3 grid((unsigned)((p.T_new + 255) / 256), (unsigned)(p.B * p.Hkv), (unsigned)M);
+  hipLaunchKernelGGL((pq_encode_kernel<D, M, KF16>), grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
 
