@@ -540,10 +540,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
                 app && wid == 1 ? D * kesz : 0);
   uint32_t kraw[8];
 
-  // Only the first chunk's codes and norms are requested before the queries arrive (a smaller burst
-  // ahead of the query loads); its V follows once the table is built.
+  // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
+  // burst streams in while the queries are rotated and the table is built.
   prologue<S, GG>(p, u, qs, lv, tid, [&] {
     fetch_codes(c, ka);
+    fetch_v(c, ka);
     const int ko = lane * 8 * kesz;
     const auto r0 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
     const auto r1 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16, 0, 0);
@@ -571,7 +572,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
   }
   S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
-  fetch_v(c, ka);
   if (lane == 0) s_prog[wid] = 0;
   lds_barrier();
 
