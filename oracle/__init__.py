@@ -216,6 +216,40 @@ def decode_attn(levels, signs, q, codes, norms, v, scale: float, seq_lens=None) 
 
 
 # --------------------------------------------------------------------------
+# Sign-pattern selection (AXELRAM key points/abstract: one-time, gradient-free
+# choice among candidate sign patterns on calibration samples)
+# --------------------------------------------------------------------------
+
+def exact_attn(q, keys, v, scale: float) -> np.ndarray:
+    """Unquantized attention [n, Hq, d] = softmax(scale * q.k) V over all T keys."""
+    q, keys, v = _f64(q), _f64(keys), _f64(v)
+    n, Hq, d = q.shape
+    _, Hkv, T, _ = keys.shape
+    out = np.zeros((n, Hq, d))
+    _load().ora_exact_attn(ctypes.c_int(d), _p(q), _p(keys), _p(v), ctypes.c_int(n), ctypes.c_int(Hq),
+                           ctypes.c_int(Hkv), ctypes.c_int64(T), ctypes.c_double(scale), _p(out))
+    return out
+
+
+def sign_errors(levels, thresholds, cands, q, keys, v, scale: float):
+    """Attention-output error of every candidate sign pattern cands [C, d]; returns (errors [C], best)."""
+    levels, thr = _f64(levels), _f64(thresholds)
+    cands = np.ascontiguousarray(np.asarray(cands, dtype=np.int8))
+    if not np.all(np.abs(cands) == 1):
+        raise ValueError("candidates must be +-1")
+    q, keys, v = _f64(q), _f64(keys), _f64(v)
+    n, Hq, d = q.shape
+    _, Hkv, T, _ = keys.shape
+    C = cands.shape[0]
+    b = levels.shape[0].bit_length() - 1
+    errors = np.zeros(C)
+    best = _load().ora_sign_errors(ctypes.c_int(d), ctypes.c_int(b), _p(levels), _p(thr), _p(cands), ctypes.c_int(C),
+                                   _p(q), _p(keys), _p(v), ctypes.c_int(n), ctypes.c_int(Hq), ctypes.c_int(Hkv),
+                                   ctypes.c_int64(T), ctypes.c_double(scale), _p(errors))
+    return errors, int(best)
+
+
+# --------------------------------------------------------------------------
 # Product quantization + ADC (LOOKAT summary/abstract)
 # --------------------------------------------------------------------------
 

@@ -34,7 +34,10 @@
  *   - a zero key has norm 0 and codes of the zero vector;
  *   - scores are raw estimates of q.k; softmax uses scale 1/sqrt(d) passed in;
  *   - grouped-query mapping: query head h reads kv head h / (Hq/Hkv);
- *   - an empty sequence (length 0) gives an all-zero attention output.
+ *   - an empty sequence (length 0) gives an all-zero attention output;
+ *   - sign-pattern selection ranks a candidate by the attention-output error
+ *     sum ||o_hat - o||^2 / sum ||o||^2 over all calibration rows (the pages
+ *     rank by perplexity, which needs a model); ties go to the lowest index.
  *
  * Everything is fp64.  Inputs arrive as double arrays (fp16/fp32 convert
  * exactly).  No blocking, no fusion, no reordering beyond the definitions.
@@ -347,6 +350,71 @@ void ora_decode_attn(int d, int b, const double* levels, const int8_t* signs, co
     }
   }
   free(s);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Sign-pattern selection.  [AX] Key Points / Abstract: the sign pattern D   */
+/* is chosen once, without gradients, among candidate patterns evaluated on  */
+/* a few calibration samples (the pages use 200 candidates and 8 samples).  */
+/* The pages rank candidates by perplexity, which needs a model; here each   */
+/* candidate is ranked by the error it causes in the attention output.       */
+/* ------------------------------------------------------------------------- */
+
+/* Exact attention, no quantization: out [n][Hq][d] = softmax(scale * q.k_t)
+ * V over all T keys, q [n][Hq][d], keys and v [n][Hkv][T][d]. */
+void ora_exact_attn(int d, const double* q, const double* keys, const double* v, int n, int Hq, int Hkv,
+                    int64_t T, double scale, double* out) {
+  const int G = Hq / Hkv;
+  double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  for (int bi = 0; bi < n; ++bi)
+    for (int h = 0; h < Hq; ++h) {
+      const int kvh = h / G;
+      const double* qh = q + ((size_t)bi * Hq + h) * d;
+      const double* kk = keys + ((size_t)bi * Hkv + kvh) * T * d;
+      for (int64_t t = 0; t < T; ++t) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += qh[i] * kk[(size_t)t * d + i];
+        s[t] = acc;
+      }
+      softmax_av(d, s, T, scale, v + ((size_t)bi * Hkv + kvh) * T * d, out + ((size_t)bi * Hq + h) * d);
+    }
+  free(s);
+}
+
+/* For every candidate pattern c (cands [C][d], each entry +-1): encode the
+ * calibration keys with it, store the norms as fp32 (as the cache does), run
+ * decode attention from the codes, and set
+ *   errors[c] = sum over rows ||o_hat - o||^2 / sum over rows ||o||^2,
+ * rows = every (sample, query head), o = exact attention.  Returns the index
+ * of the smallest error; ties go to the lowest index. */
+int ora_sign_errors(int d, int b, const double* levels, const double* thresholds, const int8_t* cands, int C,
+                    const double* q, const double* keys, const double* v, int n, int Hq, int Hkv, int64_t T,
+                    double scale, double* errors) {
+  const size_t nkeys = (size_t)n * Hkv * T;
+  const size_t nout = (size_t)n * Hq * d;
+  uint8_t* codes = (uint8_t*)malloc((size_t)d * b / 8 * (nkeys > 0 ? nkeys : 1));
+  double* norms = (double*)malloc(sizeof(double) * (nkeys > 0 ? nkeys : 1));
+  double* o = (double*)malloc(sizeof(double) * nout);
+  double* oh = (double*)malloc(sizeof(double) * nout);
+  ora_exact_attn(d, q, keys, v, n, Hq, Hkv, T, scale, o);
+  double den = 0.0;
+  for (size_t i = 0; i < nout; ++i) den += o[i] * o[i];
+  int best = 0;
+  for (int c = 0; c < C; ++c) {
+    const int8_t* sg = cands + (size_t)c * d;
+    ora_encode_keys(d, b, thresholds, sg, keys, (int64_t)nkeys, codes, norms, NULL, NULL, 0.0);
+    for (size_t r = 0; r < nkeys; ++r) norms[r] = (double)(float)norms[r];
+    ora_decode_attn(d, b, levels, sg, q, codes, norms, v, n, Hq, Hkv, T, NULL, scale, oh);
+    double num = 0.0;
+    for (size_t i = 0; i < nout; ++i) num += (oh[i] - o[i]) * (oh[i] - o[i]);
+    errors[c] = den > 0.0 ? num / den : 0.0;
+    if (errors[c] < errors[best]) best = c;
+  }
+  free(oh);
+  free(o);
+  free(norms);
+  free(codes);
+  return best;
 }
 
 /* ------------------------------------------------------------------------- */

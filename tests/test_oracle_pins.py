@@ -527,3 +527,59 @@ def test_workloads_are_deterministic_and_sliceable():
     s = W.signs(sh)
     assert set(np.unique(s)) <= {-1, 1}
     assert a.dtype == np.float16
+
+
+# ------------------------------------------------------------------------------------------------
+# Sign-pattern selection (AXELRAM key points / abstract: a one-time, gradient-free choice among
+# candidate sign patterns on a few calibration samples; ranked here by attention-output error)
+# ------------------------------------------------------------------------------------------------
+
+def _signsel_case(seed, d=16, b=2, n=2, G=2, Hkv=2, T=40, C=6):
+    rng = np.random.default_rng(seed)
+    Hq = Hkv * G
+    cands = (rng.integers(0, 2, (C, d)) * 2 - 1).astype(np.int8)
+    chan = np.exp(rng.standard_normal((Hkv, d)))  # heterogeneous channel norms
+    q = rng.standard_normal((n, Hq, d)) * 2
+    keys = rng.standard_normal((n, Hkv, T, d)) * chan[None, :, None, :]
+    v = rng.standard_normal((n, Hkv, T, d))
+    return cands, q, keys, v, G
+
+
+def test_exact_attn_equals_torch_sdpa(oracle_mod):
+    cands, q, keys, v, G = _signsel_case(1, d=32, G=4)
+    scale = 1.0 / math.sqrt(32)
+    np.testing.assert_allclose(oracle_mod.exact_attn(q, keys, v, scale), _torch_sdpa(q, keys, v, scale, G),
+                               rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("d,b", [(16, 2), (64, 4)])
+def test_sign_errors_by_an_independent_route(oracle_mod, d, b):
+    """Each candidate's error recomputed from the inverse-transform dequantization (scipy's Hadamard) and
+    torch's attention on the dequantized and on the exact keys; the selection is the first minimum."""
+    cands, q, keys, v, G = _signsel_case(7 * d + b, d=d, b=b)
+    scale = 1.0 / math.sqrt(d)
+    lv, th = oracle_mod.codebook(d, b)
+    errors, best = oracle_mod.sign_errors(lv, th, cands, q, keys, v, scale)
+    o = _torch_sdpa(q, keys, v, scale, G)
+    for c in range(len(cands)):
+        codes, norms, _, _ = oracle_mod.encode_keys(th, cands[c], keys, b)
+        norms32 = norms.astype(np.float32).astype(np.float64)  # the cache stores fp32 norms
+        khat = _dequant_original_domain(codes, norms32, cands[c], lv, d, b, oracle_mod)
+        oh = _torch_sdpa(q, khat, v, scale, G)
+        ref = np.sum((oh - o) ** 2) / np.sum(o ** 2)
+        np.testing.assert_allclose(errors[c], ref, rtol=1e-9)
+    assert best == int(np.argmin(errors))
+    assert np.all(errors > 0) and np.all(errors < 1)
+
+
+def test_sign_errors_unchanged_by_negating_the_pattern(oracle_mod):
+    """-D mirrors every code and the symmetric codebook mirrors every level, so the dequantized keys, the
+    scores and the error are exactly those of D; the tie goes to the lower index."""
+    cands, q, keys, v, G = _signsel_case(3, d=64, b=3, C=3)
+    cands = np.stack([cands[0], -cands[0], cands[1], -cands[1]])
+    lv, th = oracle_mod.codebook(64, 3)
+    errors, best = oracle_mod.sign_errors(lv, th, cands, q, keys, v, 0.125)
+    assert errors[0] == errors[1] and errors[2] == errors[3]
+    assert best in (0, 2)
+    single, b1 = oracle_mod.sign_errors(lv, th, cands[1:2], q, keys, v, 0.125)
+    assert b1 == 0 and single[0] == errors[1]

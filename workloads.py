@@ -20,6 +20,12 @@ models and datasets the pages measure on):
                  z ~ N(0, I) and sigma_t ~ LogNormal(0, 0.5) per key; q, v ~ N(0,1);
                  all fp16.
 * ``sweep``      llama8b shapes with b in {2,3,4}, B in {1,16,64}, T=8192.
+* ``signsel``    sign-pattern selection: 200 candidate patterns (+-1 with
+                 probability 1/2 each) scored on 8 calibration samples of
+                 llama8b-like shapes (Hq=32, Hkv=8, d=128, b=4) with T=512 keys
+                 each; keys and values N(0,1) times per-(kv head, channel)
+                 LogNormal(0,1) scales, the channel-norm heterogeneity under
+                 which the sign pattern matters; fp16.
 * ``pq_gpt2``    PQ-ADC with GPT-2-small-like shapes: H=12 (Hq=Hkv), d=64, m=8,
                  K=256, B=4, T=1024; q, k, v ~ N(0,1) fp16; k-means training set
                  4096 fresh N(0,1) keys per head, start rows = first K entries of
@@ -62,6 +68,9 @@ LLAMA8B = Shape("llama8b", B=1, Hq=32, Hkv=8, d=128, T=4096, b=4, key_scale="cha
 LONGCTX = Shape("longctx", B=8, Hq=32, Hkv=4, d=64, T=32768, b=4, key_scale="token_lognormal",
                 seed=SEED_BASE + 2)
 PQ_GPT2 = Shape("pq_gpt2", B=4, Hq=12, Hkv=12, d=64, T=1024, m=8, K=256, seed=SEED_BASE + 4)
+SIGNSEL = Shape("signsel", B=8, Hq=32, Hkv=8, d=128, T=512, b=4, key_scale="channel_lognormal",
+                v_scale="channel_lognormal", seed=SEED_BASE + 5)
+SIGN_CANDIDATES = 200
 
 
 def sweep(b: int, B: int) -> Shape:
@@ -81,14 +90,21 @@ def _children(seed: int, n: int):
 
 
 # child slots: 0 signs, 1 q, 2 key scales, 3 keys (per batch), 4 value scales, 5 values (per batch),
-#              6 PQ training set, 7 PQ start rows, 8 new keys for the write path (per batch)
-_SLOTS = 9
+#              6 PQ training set, 7 PQ start rows, 8 new keys for the write path (per batch),
+#              9 candidate sign patterns
+_SLOTS = 10
 
 
 def signs(shape: Shape) -> np.ndarray:
     """The +-1 sign pattern D, each entry +1 or -1 with probability 1/2."""
     rng = np.random.default_rng(_children(shape.seed, _SLOTS)[0])
     return (rng.integers(0, 2, size=shape.d, dtype=np.int8) * 2 - 1).astype(np.int8)
+
+
+def sign_candidates(shape: Shape, C: int = SIGN_CANDIDATES) -> np.ndarray:
+    """C candidate sign patterns [C, d], each entry +1 or -1 with probability 1/2."""
+    rng = np.random.default_rng(_children(shape.seed, _SLOTS)[9])
+    return (rng.integers(0, 2, size=(C, shape.d), dtype=np.int8) * 2 - 1).astype(np.int8)
 
 
 def queries(shape: Shape) -> np.ndarray:
