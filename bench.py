@@ -252,6 +252,33 @@ def run_suite(K, torch, reps=5, calls=30):
     row("pq_gpt2", "decode", timed(pq_dec, n_rot), nkeys * (m + 2 * d) + B * H * d * 2, nkeys, nkeys)
     row("pq_gpt2", "score", timed(pq_score, n_rot), nkeys * (m + 4), nkeys, nkeys)
     row("pq_gpt2", "encode", timed(pq_enc, n_rot), nkeys * (2 * d + m), 0, nkeys)
+    del caches, keys, vals
+    torch.cuda.empty_cache()
+
+    # one-time sign-pattern selection: 200 candidates on 8 calibration samples of 512 keys.  The call is
+    # synchronous (it returns the ranking to the host), so it is timed by wall clock, not in a graph; the
+    # row reports the time per candidate (an encode and a decode of the calibration keys plus the error).
+    sh = W.SIGNSEL
+    B, Hq, Hkv, d, T, b = sh.B, sh.Hq, sh.Hkv, sh.d, sh.T, sh.b
+    cb = K.kvq_build_codebook(d, b)
+    cands = W.sign_candidates(sh)
+    C = cands.shape[0]
+    q, keys, vals = rnd(B, Hq, d).half(), draw_keys(sh, T), draw_values(sh, T)
+    ws = torch.empty(K.kvq_select_signs_workspace(cb, B, Hq, Hkv, T, C), dtype=torch.uint8, device=dev)
+    K.kvq_select_signs(cb, cands, q, keys, vals, workspace=ws)
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        K.kvq_select_signs(cb, cands, q, keys, vals, workspace=ws)
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    sel = ts[len(ts) // 2]
+    nkeys = B * Hkv * T
+    bpk = cb.bytes_per_key
+    per_cand = nkeys * (2 * d + bpk + 4) + nkeys * (bpk + 4 + 2 * d) + 2 * B * Hq * d * 4
+    row("signsel_200", "select/cand", sel / C, per_cand, B * Hq * T, nkeys)
+    eprint("signsel_200: whole selection %.2f ms for %d candidates" % (sel * 1e3, C))
     return rows
 
 

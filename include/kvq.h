@@ -207,6 +207,35 @@ kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, c
                                   const int32_t* seq_lens, float scale, void* out, kvq_dtype odtype,
                                   void* workspace, size_t ws_bytes, int n_splits, void* stream);
 
+/* Bytes of device workspace kvq_select_signs needs (0 on invalid arguments or
+ * a PQ codebook). */
+size_t kvq_select_signs_workspace(const kvq_codebook* cb, int n_cal, int Hq, int Hkv, int64_t T, int C);
+
+/* One-time choice of the sign pattern D (AXELRAM, Key Points / Abstract: a
+ * gradient-free selection among candidate sign patterns, evaluated once on a
+ * few calibration samples).  The pages rank candidates by perplexity, which
+ * needs a model; here candidate c is ranked by the attention-output error it
+ * causes:
+ *   errors[c] = sum ||o_c - o||^2 / sum ||o||^2 over every (sample, query head),
+ * o = exact attention (fp32, no quantization), o_c = kvq_decode_attn of the
+ * calibration keys encoded with pattern c (kvq_encode_keys, same codebook).
+ *   candidates: host [C][d] int8, each entry +1 or -1.
+ *   q: device [n_cal][Hq][d]; keys, v: device [n_cal][Hkv][T][d] (dtypes as
+ *      given, 16-byte aligned), 1 <= T <= 8192.
+ *   scale: softmax scale.
+ *   errors: host [C] fp32, written.  best: host, the index of the smallest
+ *      error (lowest index on ties), written.
+ *   workspace: device, >= kvq_select_signs_workspace(...) bytes, 256-byte
+ *      aligned; its contents on entry do not matter.
+ * Synchronous: the call waits for `stream` before it returns.
+ * Errors: KVQ_ERR_INVALID_ARG (sizes, NULL, misaligned, a candidate entry not
+ *   +-1), KVQ_ERR_UNSUPPORTED (PQ codebook, T out of range), KVQ_ERR_WORKSPACE,
+ *   KVQ_ERR_DEVICE. */
+kvq_status kvq_select_signs(const kvq_codebook* cb, const int8_t* candidates, int C, const void* q,
+                            kvq_dtype qdtype, const void* keys, kvq_dtype kdtype, const void* v, kvq_dtype vdtype,
+                            int n_cal, int Hq, int Hkv, int64_t T, float scale, float* errors, int* best,
+                            void* workspace, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -387,3 +387,123 @@ kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, c
 }
 
 }  // extern "C"
+
+namespace {
+
+size_t pad256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of kvq_select_signs: exact output, decode output, candidate errors, codes, norms, and the
+// decode's own workspace, each 256-byte aligned.
+struct SelectLayout {
+  size_t exact, dec, err, codes, norms, dws, total, dws_bytes;
+};
+
+bool select_layout(const kvq_codebook* cb, int n, int Hq, int Hkv, int64_t T, int C, SelectLayout* L) {
+  if (check_codebook(cb) != KVQ_OK || cb->kind != KVQ_HADAMARD_LM || n <= 0 || Hq <= 0 || Hkv <= 0 ||
+      Hq % Hkv != 0 || T <= 0 || C <= 0)
+    return false;
+  const size_t outb = (size_t)n * Hq * cb->d * 4;
+  const size_t nkeys = (size_t)n * Hkv * T;
+  L->exact = 0;
+  L->dec = L->exact + pad256(outb);
+  L->err = L->dec + pad256(outb);
+  L->codes = L->err + pad256((size_t)C * 4);
+  L->norms = L->codes + pad256(nkeys * (size_t)(cb->d * cb->b / 8));
+  L->dws = L->norms + pad256(nkeys * 4);
+  L->dws_bytes = kvq_decode_attn_workspace(cb, n, Hq, Hkv, T, 0);
+  L->total = L->dws + pad256(L->dws_bytes);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_select_signs_workspace(const kvq_codebook* cb, int n_cal, int Hq, int Hkv, int64_t T, int C) {
+  SelectLayout L;
+  return select_layout(cb, n_cal, Hq, Hkv, T, C, &L) ? L.total : 0;
+}
+
+kvq_status kvq_select_signs(const kvq_codebook* cb, const int8_t* candidates, int C, const void* q,
+                            kvq_dtype qdtype, const void* keys, kvq_dtype kdtype, const void* v, kvq_dtype vdtype,
+                            int n_cal, int Hq, int Hkv, int64_t T, float scale, float* errors, int* best,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  kvq_status st = check_codebook(cb);
+  if (st != KVQ_OK) return st;
+  if (cb->kind != KVQ_HADAMARD_LM) return fail(KVQ_ERR_UNSUPPORTED, "sign patterns belong to the Hadamard codec");
+  if (!candidates || C <= 0) return fail(KVQ_ERR_INVALID_ARG, "need at least one candidate pattern");
+  if (!errors || !best) return fail(KVQ_ERR_INVALID_ARG, "errors or best is NULL");
+  if (n_cal <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "n_cal=%d Hq=%d Hkv=%d", n_cal, Hq, Hkv);
+  if (T <= 0 || T > kvq::kCalibMaxT)
+    return fail(KVQ_ERR_UNSUPPORTED, "T=%lld: calibration samples hold 1..%d keys", (long long)T, kvq::kCalibMaxT);
+  if (!valid_dtype(qdtype) || !valid_dtype(kdtype) || !valid_dtype(vdtype))
+    return fail(KVQ_ERR_INVALID_ARG, "bad dtype");
+  if (!q || !keys || !v) return fail(KVQ_ERR_INVALID_ARG, "q, keys or v is NULL");
+  if (!aligned16(q) || !aligned16(keys) || !aligned16(v))
+    return fail(KVQ_ERR_INVALID_ARG, "q, keys or v not 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(KVQ_ERR_INVALID_ARG, "scale is not finite");
+  uint32_t packed[8];
+  for (int c = 0; c < C; ++c) {
+    st = pack_signs(candidates + (size_t)c * cb->d, cb->d, packed);
+    if (st != KVQ_OK) {
+      const std::string why = g_last_error;
+      return fail(KVQ_ERR_INVALID_ARG, "candidate %d: %s", c, why.c_str());
+    }
+  }
+  SelectLayout L;
+  select_layout(cb, n_cal, Hq, Hkv, T, C, &L);
+  if (!workspace || ws_bytes < L.total)
+    return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  char* ws = reinterpret_cast<char*>(workspace);
+  float* exact = reinterpret_cast<float*>(ws + L.exact);
+  float* dec = reinterpret_cast<float*>(ws + L.dec);
+  float* err_dev = reinterpret_cast<float*>(ws + L.err);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + L.codes);
+  float* norms = reinterpret_cast<float*>(ws + L.norms);
+  void* dws = L.dws_bytes ? ws + L.dws : nullptr;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // the decode's arrival counters must start at zero (a fill kernel, not a memset)
+  if (L.dws_bytes) {
+    st = from_hip(kvq::launch_zero_words(reinterpret_cast<uint32_t*>(dws), L.dws_bytes / 4, s), "kvq_select_signs");
+    if (st != KVQ_OK) return st;
+  }
+
+  kvq::CalibParams cp;
+  cp.q = q;
+  cp.keys = keys;
+  cp.v = v;
+  cp.out = exact;
+  cp.n = n_cal;
+  cp.Hq = Hq;
+  cp.Hkv = Hkv;
+  cp.T = (int)T;
+  cp.q_f16 = qdtype == KVQ_F16;
+  cp.k_f16 = kdtype == KVQ_F16;
+  cp.v_f16 = vdtype == KVQ_F16;
+  cp.scale = scale;
+  st = from_hip(kvq::launch_exact_attn(cb->d, cp, s), "kvq_select_signs");
+  if (st != KVQ_OK) return st;
+  const int64_t nout = (int64_t)n_cal * Hq * cb->d;
+  for (int c = 0; c < C; ++c) {
+    const int8_t* sg = candidates + (size_t)c * cb->d;
+    st = kvq_encode_keys(cb, sg, keys, kdtype, n_cal, Hkv, T, codes, norms, T, 0, nullptr, stream);
+    if (st != KVQ_OK) return st;
+    st = kvq_decode_attn(cb, sg, q, qdtype, codes, norms, v, vdtype, n_cal, Hq, Hkv, T, nullptr, scale, dec, KVQ_F32,
+                         dws, L.dws_bytes, 0, stream);
+    if (st != KVQ_OK) return st;
+    st = from_hip(kvq::launch_rel_err(dec, exact, nout, err_dev, c, s), "kvq_select_signs");
+    if (st != KVQ_OK) return st;
+  }
+  if (hipMemcpyAsync(errors, err_dev, (size_t)C * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(KVQ_ERR_DEVICE, "kvq_select_signs: reading the errors back failed");
+  int b = 0;
+  for (int c = 1; c < C; ++c)
+    if (errors[c] < errors[b]) b = c;
+  *best = b;
+  return ok();
+}
+
+}  // extern "C"

@@ -88,6 +88,21 @@ hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, 
 hipError_t launch_hlm_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
 hipError_t launch_pq_encode(int D, int M, bool k_f16, const EncodeParams& p, hipStream_t s);
 
+// Exact attention over calibration samples (sign-pattern selection).
+constexpr int kCalibMaxT = 8192;  // keys per calibration sample (scores held in LDS)
+struct CalibParams {
+  const void* q;     // [n][Hq][D]
+  const void* keys;  // [n][Hkv][T][D]
+  const void* v;     // [n][Hkv][T][D]
+  float* out;        // [n][Hq][D] fp32
+  int n, Hq, Hkv, T;
+  int q_f16, k_f16, v_f16;
+  float scale;
+};
+hipError_t launch_exact_attn(int D, const CalibParams& p, hipStream_t s);
+hipError_t launch_rel_err(const float* oh, const float* o, int64_t n, float* errors, int c, hipStream_t s);
+hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
+
 // Cell grid for the encode's threshold search (codebook.cpp); false if none fits kEncodeMaxCells.
 bool choose_encode_cells(const float* thresholds, int n_thresholds, int* n_cells, float* cell_inv, float* cell_shift);
 

@@ -77,12 +77,17 @@ _lib.kvq_decode_attn.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32
                                  _P, _i32, _P, _sz, _i32, _P]
 _lib.kvq_decode_attn_append.argtypes = [_CB, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P,
                                         _f32, _P, _i32, _P, _sz, _i32, _P]
+_lib.kvq_select_signs_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
+_lib.kvq_select_signs_workspace.restype = _sz
+_lib.kvq_select_signs.argtypes = [_CB, _P, _i32, _P, _i32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i64, _f32, _P, _P,
+                                  _P, _sz, _P]
 for _f in ("kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
-           "kvq_decode_attn", "kvq_decode_attn_append"):
+           "kvq_decode_attn", "kvq_decode_attn_append", "kvq_select_signs"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq",
-           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append")
+           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append",
+           "kvq_select_signs_workspace", "kvq_select_signs")
 
 
 def _check(status: int):
@@ -244,3 +249,31 @@ def kvq_decode_attn_append(cb: kvq_codebook, signs, new_keys: torch.Tensor, q: t
                                        _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
                                        _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
     return out
+
+
+def kvq_select_signs_workspace(cb: kvq_codebook, n_cal: int, Hq: int, Hkv: int, T: int, C: int) -> int:
+    return int(_lib.kvq_select_signs_workspace(ctypes.byref(cb), n_cal, Hq, Hkv, T, C))
+
+
+def kvq_select_signs(cb: kvq_codebook, candidates, q: torch.Tensor, keys: torch.Tensor, v: torch.Tensor,
+                     scale: float | None = None, workspace=None, stream=None):
+    """Rank candidate sign patterns [C][d] on calibration q [n][Hq][d], keys/v [n][Hkv][T][d]: (errors, best)."""
+    n, Hq, d = q.shape
+    _, Hkv, T, _ = keys.shape
+    cand = np.ascontiguousarray(np.asarray(candidates.cpu() if isinstance(candidates, torch.Tensor) else candidates,
+                                           dtype=np.int8))
+    if cand.ndim != 2 or cand.shape[1] != d:
+        raise ValueError("candidates must have shape (C, %d)" % d)
+    C = cand.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = kvq_select_signs_workspace(cb, n, Hq, Hkv, T, C)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    errors = np.zeros(C, dtype=np.float32)
+    best = ctypes.c_int(-1)
+    _check(_lib.kvq_select_signs(ctypes.byref(cb), cand.ctypes.data_as(_P), C, _dev(q, "q"), _dt(q),
+                                 _dev(keys, "keys"), _dt(keys), _dev(v, "v"), _dt(v), n, Hq, Hkv, T, float(scale),
+                                 errors.ctypes.data_as(_P), ctypes.byref(best), _dev(workspace, "workspace"),
+                                 workspace.numel(), _stream(stream)))
+    return errors, int(best.value)

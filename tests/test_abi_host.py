@@ -194,3 +194,37 @@ def test_offset_limit(K):
     s = np.ones(256, dtype=np.int8)
     assert _call_decode(K, cb, s, T_cap=(1 << 31) // (4 * 256)) == K.KVQ_ERR_UNSUPPORTED
     assert "32-bit" in K.kvq_last_error()
+
+
+def test_select_signs_validation_and_workspace(K):
+    P = ctypes.c_void_p
+    cb = K.kvq_build_codebook(64, 4)
+    lib = K._lib
+    cands = np.ones((3, 64), dtype=np.int8)
+    errs = np.zeros(3, dtype=np.float32)
+    best = ctypes.c_int(-7)
+    need = K.kvq_select_signs_workspace(cb, 2, 4, 2, 100, 3)
+    # exact + decoded outputs, errors, codes, norms (each padded to 256 bytes); one split needs no decode workspace
+    assert need == 2 * 2048 + 256 + 12800 + 1792
+    assert K.kvq_select_signs_workspace(cb, 2, 3, 2, 100, 3) == 0
+
+    def call(cbx=cb, c=cands, C=3, T=100, ws=FAKE, ws_bytes=need, qdt=1, e=errs):
+        return lib.kvq_select_signs(ctypes.byref(cbx), c.ctypes.data_as(P), C, P(FAKE), qdt, P(FAKE), 1, P(FAKE), 1,
+                                    2, 4, 2, T, 0.125, None if e is None else e.ctypes.data_as(P), ctypes.byref(best),
+                                    P(ws), ws_bytes, None)
+    bad = cands.copy()
+    bad[2, 5] = 0
+    assert call(c=bad) == K.KVQ_ERR_INVALID_ARG
+    assert "candidate 2" in K.kvq_last_error()
+    assert call(C=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(e=None) == K.KVQ_ERR_INVALID_ARG
+    assert call(qdt=9) == K.KVQ_ERR_INVALID_ARG
+    assert call(T=0) == K.KVQ_ERR_UNSUPPORTED
+    assert call(T=8193) == K.KVQ_ERR_UNSUPPORTED
+    assert call(ws_bytes=need - 1) == K.KVQ_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == K.KVQ_ERR_INVALID_ARG
+    assert "256-byte" in K.kvq_last_error()
+    pq = K.kvq_codebook()
+    K._check(lib.kvq_codebook_pq(64, 8, 256, 2, P(FAKE), ctypes.byref(pq)))
+    assert call(cbx=pq) == K.KVQ_ERR_UNSUPPORTED
+    assert best.value == -7  # nothing written on failure
