@@ -216,6 +216,50 @@ def decode_attn(levels, signs, q, codes, norms, v, scale: float, seq_lens=None) 
 
 
 # --------------------------------------------------------------------------
+# Values quantized with the key codec (a reading: the value row is encoded as a
+# key is, and attention uses v_hat = |v| D H^T c_hat)
+# --------------------------------------------------------------------------
+
+def dequant(levels, signs, codes, norms) -> np.ndarray:
+    """Rows [..., d] = norm * D H^T c_hat of code rows [..., bpk] with norms [...]."""
+    levels = _f64(levels)
+    signs = _signs(signs)
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    lead = codes.shape[:-1]
+    b = levels.shape[0].bit_length() - 1
+    d = codes.shape[-1] * 8 // b
+    norms = _f64(norms)
+    assert norms.shape == lead
+    n = int(np.prod(lead)) if lead else 1
+    out = np.zeros(lead + (d,))
+    _load().ora_dequant_rows(ctypes.c_int(d), ctypes.c_int(b), _p(levels), _p(signs), _p(codes), _p(norms),
+                             ctypes.c_int64(n), _p(out))
+    return out
+
+
+def decode_attn_qv(levels, signs, q, codes, norms, vcodes, vnorms, scale: float, seq_lens=None) -> np.ndarray:
+    """Attention output [B, Hq, d] with keys and values both as codes + norms [B, Hkv, T, ...]."""
+    levels = _f64(levels)
+    signs = _signs(signs)
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    vcodes = np.ascontiguousarray(np.asarray(vcodes, dtype=np.uint8))
+    _, Hkv, T, bpk = codes.shape
+    b = levels.shape[0].bit_length() - 1
+    assert bpk == d * b // 8 and vcodes.shape == codes.shape
+    norms, vnorms = _f64(norms), _f64(vnorms)
+    assert norms.shape == (B, Hkv, T) and vnorms.shape == (B, Hkv, T)
+    lens = _lens(seq_lens, B)
+    out = np.zeros((B, Hq, d))
+    _load().ora_decode_attn_qv(ctypes.c_int(d), ctypes.c_int(b), _p(levels), _p(signs), _p(q), _p(codes),
+                               _p(norms), _p(vcodes), _p(vnorms), ctypes.c_int(B), ctypes.c_int(Hq),
+                               ctypes.c_int(Hkv), ctypes.c_int64(T), None if lens is None else _p(lens),
+                               ctypes.c_double(scale), _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------
 # Sign-pattern selection (AXELRAM key points/abstract: one-time, gradient-free
 # choice among candidate sign patterns on calibration samples)
 # --------------------------------------------------------------------------

@@ -35,6 +35,8 @@
  *   - scores are raw estimates of q.k; softmax uses scale 1/sqrt(d) passed in;
  *   - grouped-query mapping: query head h reads kv head h / (Hq/Hkv);
  *   - an empty sequence (length 0) gives an all-zero attention output;
+ *   - quantized values: a value row is encoded exactly as a key is, and the
+ *     attention output uses the dequantized rows ||v|| D H^T c_hat;
  *   - sign-pattern selection ranks a candidate by the attention-output error
  *     sum ||o_hat - o||^2 / sum ||o||^2 over all calibration rows (the pages
  *     rank by perplexity, which needs a model); ties go to the lowest index.
@@ -350,6 +352,48 @@ void ora_decode_attn(int d, int b, const double* levels, const int8_t* signs, co
     }
   }
   free(s);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Values quantized with the key codec.  [AX] Abstract quantizes keys only;  */
+/* [SA] English abstract quantizes values too, in its own codec.  Reading:   */
+/* a value row is encoded exactly as a key is (its norm and the b-bit codes  */
+/* of H D v / ||v||, ora_encode_keys), and attention uses the dequantized    */
+/* rows v_hat = ||v|| (H D)^T c_hat = ||v|| D H^T c_hat.                     */
+/* ------------------------------------------------------------------------- */
+
+/* Dequantize n rows: out[r] = norms[r] * D * H^T * c_hat(row r), with
+ * c_hat_i = levels[code_i], as an explicit matrix product. */
+void ora_dequant_rows(int d, int b, const double* levels, const int8_t* signs, const uint8_t* codes,
+                      const double* norms, int64_t n, double* out) {
+  const int bpk = d * b / 8;
+  double* H = (double*)malloc(sizeof(double) * (size_t)d * d);
+  double* c = (double*)malloc(sizeof(double) * (size_t)d);
+  ora_hadamard(d, H);
+  for (int64_t r = 0; r < n; ++r) {
+    const uint8_t* row = codes + (size_t)r * bpk;
+    for (int i = 0; i < d; ++i) c[i] = levels[get_code(row, i, b)];
+    for (int j = 0; j < d; ++j) {
+      double acc = 0.0; /* (H^T c)_j = sum_i H[i][j] c_i */
+      for (int i = 0; i < d; ++i) acc += H[(size_t)i * d + j] * c[i];
+      out[(size_t)r * d + j] = norms[r] * (double)signs[j] * acc;
+    }
+  }
+  free(c);
+  free(H);
+}
+
+/* Decode attention with quantized values: the keys score as in
+ * ora_decode_attn, and V is the dequantized cache of (vcodes, vnorms). */
+void ora_decode_attn_qv(int d, int b, const double* levels, const int8_t* signs, const double* q,
+                        const uint8_t* codes, const double* norms, const uint8_t* vcodes,
+                        const double* vnorms, int B, int Hq, int Hkv, int64_t Tcap,
+                        const int32_t* seq_lens, double scale, double* out) {
+  const int64_t rows = (int64_t)B * Hkv * Tcap;
+  double* v = (double*)malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1) * d);
+  ora_dequant_rows(d, b, levels, signs, vcodes, vnorms, rows, v);
+  ora_decode_attn(d, b, levels, signs, q, codes, norms, v, B, Hq, Hkv, Tcap, seq_lens, scale, out);
+  free(v);
 }
 
 /* ------------------------------------------------------------------------- */

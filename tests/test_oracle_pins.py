@@ -583,3 +583,84 @@ def test_sign_errors_unchanged_by_negating_the_pattern(oracle_mod):
     assert best in (0, 2)
     single, b1 = oracle_mod.sign_errors(lv, th, cands[1:2], q, keys, v, 0.125)
     assert b1 == 0 and single[0] == errors[1]
+
+
+# ----------------------------------------------------------------------------------------------
+# Values quantized with the key codec
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,b", [(16, 1), (64, 4), (128, 3), (256, 2)])
+def test_dequant_equals_inverse_transform_by_scipy(oracle_mod, d, b):
+    rng = np.random.default_rng(5 * d + b)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    v = rng.standard_normal((3, 11, d)) * rng.lognormal(0, 1, size=(3, 11, 1))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, v, b)
+    got = oracle_mod.dequant(lv, s, codes, norms)
+    ref = _dequant_original_domain(codes, norms, s, lv, d, b, oracle_mod)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("b", [1, 2, 3, 4])
+def test_dequant_distortion_matches_the_quantizer(oracle_mod, b):
+    """E|v/|v| - v_hat/|v||^2 ~= MSE_b of the unit Lloyd-Max quantizer (d coordinates of variance 1/d),
+    and the reconstruction is unbiased in direction: E<u, u_hat> ~= 1 - MSE_b (centroid condition)."""
+    d = 128
+    rng = np.random.default_rng(40 + b)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    v = rng.standard_normal((3000, d)) * 3.0
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, v, b)
+    vh = oracle_mod.dequant(lv, s, codes, norms)
+    u = v / norms[:, None]
+    uh = vh / norms[:, None]
+    c, t, _ = oracle_mod.lloyd_max_unit(b)
+    mse = oracle_mod.quantizer_mse_unit(b, c, t)
+    assert np.mean(np.sum((u - uh) ** 2, axis=1)) == pytest.approx(mse, rel=0.05)
+    assert np.mean(np.sum(u * uh, axis=1)) == pytest.approx(1.0 - mse, rel=0.01)
+
+
+@pytest.mark.parametrize("d,b,G", [(16, 2, 1), (64, 4, 8), (128, 3, 4)])
+def test_decode_attn_qv_equals_sdpa_on_dequantized_keys_and_values(oracle_mod, d, b, G):
+    rng = np.random.default_rng(7 * d + b + G)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    B, Hkv, T = 2, 2, 45
+    Hq = Hkv * G
+    q = rng.standard_normal((B, Hq, d)) * 3
+    keys = rng.standard_normal((B, Hkv, T, d)) * 2
+    v = rng.standard_normal((B, Hkv, T, d)) * rng.lognormal(0, 1, size=(1, Hkv, 1, d))
+    lv, th = oracle_mod.codebook(d, b)
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    vcodes, vnorms, _, _ = oracle_mod.encode_keys(th, s, v, b)
+    scale = 1.0 / math.sqrt(d)
+    lens = [T, 17]
+    out = oracle_mod.decode_attn_qv(lv, s, q, codes, norms, vcodes, vnorms, scale, seq_lens=lens)
+    khat = _dequant_original_domain(codes, norms, s, lv, d, b, oracle_mod)
+    vhat = _dequant_original_domain(vcodes, vnorms, s, lv, d, b, oracle_mod)
+    for bi, n in enumerate(lens):
+        ref = _torch_sdpa(q[bi:bi + 1], khat[bi:bi + 1, :, :n], vhat[bi:bi + 1, :, :n], scale, G)
+        np.testing.assert_allclose(out[bi:bi + 1], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_decode_attn_qv_special_cases(oracle_mod):
+    """One value row repeated at every position: the output is that row's reconstruction whatever the
+    scores; an empty sequence gives zeros; a zero value row reconstructs to zero."""
+    d, b = 64, 4
+    rng = np.random.default_rng(12)
+    s = W.signs(W.LONGCTX)
+    lv, th = oracle_mod.codebook(d, b)
+    T = 30
+    q = rng.standard_normal((2, 2, d)) * 5
+    keys = rng.standard_normal((2, 1, T, d)) * 3
+    row = rng.standard_normal(d) * 2
+    v = np.broadcast_to(row, (2, 1, T, d)).copy()
+    v[1] = 0.0
+    codes, norms, _, _ = oracle_mod.encode_keys(th, s, keys, b)
+    vcodes, vnorms, _, _ = oracle_mod.encode_keys(th, s, v, b)
+    out = oracle_mod.decode_attn_qv(lv, s, q, codes, norms, vcodes, vnorms, 0.125, seq_lens=[T, T])
+    rc, rn, _, _ = oracle_mod.encode_keys(th, s, row[None, :], b)
+    rhat = oracle_mod.dequant(lv, s, rc, rn)[0]
+    np.testing.assert_allclose(out[0], np.broadcast_to(rhat, (2, d)), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(out[1], 0.0)
+    out0 = oracle_mod.decode_attn_qv(lv, s, q, codes, norms, vcodes, vnorms, 0.125, seq_lens=[0, 5])
+    np.testing.assert_array_equal(out0[0], 0.0)
