@@ -207,6 +207,25 @@ kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, c
                                   const int32_t* seq_lens, float scale, void* out, kvq_dtype odtype,
                                   void* workspace, size_t ws_bytes, int n_splits, void* stream);
 
+/* Decode attention with the values quantized too (an extension of the key
+ * codec of AXELRAM, Abstract, to V; the shift-accumulate attention page,
+ * English abstract, quantizes V in its own codec).  The value rows are encoded
+ * by kvq_encode_keys with the same codebook and signs (vcodes, vnorms have the
+ * layout of codes, norms), and the output is
+ *   out[b][h] = sum_t p_t * |v_t| * D H^T c_hat(v_t) / sum_t p_t
+ * with p_t the softmax weights of kvq_decode_attn.  The weighted sum is taken
+ * in the rotated domain and D H^T is applied once per query head.
+ *   vcodes: device [B][Hkv][T_cap][d*b/8], vnorms: device [B][Hkv][T_cap]
+ *   fp32, both 16-byte aligned.  Every other argument, the workspace
+ *   (kvq_decode_attn_workspace) and the errors are those of kvq_decode_attn.
+ *   The products run in fp16 with fp32 accumulation: |v_t| times a level
+ *   must stay within the fp16 range.
+ * Hadamard/Lloyd-Max codebooks only (KVQ_ERR_UNSUPPORTED for PQ). */
+kvq_status kvq_decode_attn_qv(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                              const uint8_t* codes, const float* norms, const uint8_t* vcodes, const float* vnorms,
+                              int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale, void* out,
+                              kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits, void* stream);
+
 /* Bytes of device workspace kvq_select_signs needs (0 on invalid arguments or
  * a PQ codebook). */
 size_t kvq_select_signs_workspace(const kvq_codebook* cb, int n_cal, int Hq, int Hkv, int64_t T, int C);

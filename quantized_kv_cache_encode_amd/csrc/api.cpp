@@ -386,6 +386,43 @@ kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, c
                        Hq, Hkv, T_cap, seq_lens, scale, out, odtype, workspace, ws_bytes, n_splits, stream);
 }
 
+kvq_status kvq_decode_attn_qv(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                              const uint8_t* codes, const float* norms, const uint8_t* vcodes, const float* vnorms,
+                              int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale, void* out,
+                              kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits, void* stream) {
+  kvq::AttnParams p;
+  ReadShape rs;
+  kvq_status st = check_read(cb, signs, q, qdtype, codes, norms, B, Hq, Hkv, T_cap, &p, &rs);
+  if (st != KVQ_OK) return st;
+  if (cb->kind != KVQ_HADAMARD_LM)
+    return fail(KVQ_ERR_UNSUPPORTED, "quantized values use the Hadamard/Lloyd-Max codec only");
+  if (!vcodes || !vnorms || !out) return fail(KVQ_ERR_INVALID_ARG, "vcodes, vnorms or out is NULL");
+  if (!aligned16(vcodes) || !aligned16(vnorms) || !aligned16(out))
+    return fail(KVQ_ERR_INVALID_ARG, "vcodes, vnorms or out not 16-byte aligned");
+  if (!valid_dtype(odtype)) return fail(KVQ_ERR_INVALID_ARG, "bad out dtype %d", (int)odtype);
+  if (n_splits < 0) return fail(KVQ_ERR_INVALID_ARG, "n_splits=%d", n_splits);
+  if (!std::isfinite(scale)) return fail(KVQ_ERR_INVALID_ARG, "scale is not finite");
+  p.vcodes = vcodes;
+  p.vnorms = vnorms;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.out_f16 = odtype == KVQ_F16;
+  p.zscale = scale * 1.4426950408889634f;
+  choose_splits(rs.units, T_cap, n_splits, &p.n_splits, &p.split_len);
+  if (p.n_splits > 1) {
+    const size_t need = workspace_bytes(rs.units, B, Hq, p.n_splits, cb->d);
+    if (!workspace || ws_bytes < need)
+      return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, need);
+    if (!aligned16(workspace)) return fail(KVQ_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    const size_t counter_bytes = ((size_t)rs.units * 4 + 255) / 256 * 256;
+    p.counters = reinterpret_cast<unsigned*>(workspace);
+    p.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counter_bytes);
+  }
+  const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
+  return from_hip(kvq::launch_hlm_decode_qv(cb->d, cb->b, rs.gg, p, grid, reinterpret_cast<hipStream_t>(stream)),
+                  "kvq_decode_attn_qv");
+}
+
 }  // extern "C"
 
 namespace {

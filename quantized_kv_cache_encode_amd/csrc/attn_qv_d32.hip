@@ -1,0 +1,6 @@
+// Decode attention over quantized keys and values, head dimension 32.
+#include "attn_qv.h"
+
+namespace kvq {
+template hipError_t run_qv_decode<32>(int, int, const AttnParams&, dim3, hipStream_t);
+}  // namespace kvq

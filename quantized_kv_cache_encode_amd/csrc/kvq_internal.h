@@ -42,6 +42,9 @@ struct AttnParams {
   float* app_norms;          // the norm cache, written at the new rows (same buffer as norms)
   int new_f16;
   float thresholds[15];
+  // values as codes of the same codec (kvq_decode_attn_qv): [B][Hkv][T_cap][bytes per key] and norms
+  const uint8_t* vcodes;
+  const float* vnorms;
 };
 
 struct EncodeParams {
@@ -82,6 +85,7 @@ constexpr int kEncodeMaxCells = 1024;
 hipError_t launch_hlm_decode(int D, int bits, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
                              hipStream_t s);
 hipError_t launch_hlm_score(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_hlm_decode_qv(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_pq_decode(int D, int M, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
                             hipStream_t s);
 hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);

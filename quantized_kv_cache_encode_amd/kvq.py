@@ -77,17 +77,19 @@ _lib.kvq_decode_attn.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32
                                  _P, _i32, _P, _sz, _i32, _P]
 _lib.kvq_decode_attn_append.argtypes = [_CB, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P,
                                         _f32, _P, _i32, _P, _sz, _i32, _P]
+_lib.kvq_decode_attn_qv.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32, _i32, _i64, _P, _f32, _P, _i32,
+                                    _P, _sz, _i32, _P]
 _lib.kvq_select_signs_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
 _lib.kvq_select_signs_workspace.restype = _sz
 _lib.kvq_select_signs.argtypes = [_CB, _P, _i32, _P, _i32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i64, _f32, _P, _P,
                                   _P, _sz, _P]
 for _f in ("kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
-           "kvq_decode_attn", "kvq_decode_attn_append", "kvq_select_signs"):
+           "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_qv", "kvq_select_signs"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq",
            "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append",
-           "kvq_select_signs_workspace", "kvq_select_signs")
+           "kvq_decode_attn_qv", "kvq_select_signs_workspace", "kvq_select_signs")
 
 
 def _check(status: int):
@@ -222,6 +224,33 @@ def kvq_decode_attn(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tenso
                                 _dev(norms, "norms", torch.float32, optional=True), _dev(v, "v"), _dt(v), B, Hq, Hkv,
                                 T_cap, _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
                                 _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
+    return out
+
+
+def kvq_decode_attn_qv(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tensor, norms: torch.Tensor,
+                       vcodes: torch.Tensor, vnorms: torch.Tensor, scale: float | None = None, seq_lens=None,
+                       out=None, out_dtype=torch.float16, workspace=None, n_splits: int = 0,
+                       stream=None) -> torch.Tensor:
+    """Attention output [B][Hq][d] with the values stored as codes + norms of the same codec."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = codes.shape
+    if tuple(vcodes.shape) != tuple(codes.shape) or tuple(vnorms.shape) != (B, Hkv, T_cap):
+        raise ValueError("vcodes / vnorms must have the shapes of codes / norms")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
+    need = kvq_decode_attn_workspace(cb, B, Hq, Hkv, T_cap, n_splits)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)  # counters start at zero
+    ws_ptr = _dev(workspace, "workspace", optional=True)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    s_np, s_ptr = _signs_host(signs, d)
+    _check(_lib.kvq_decode_attn_qv(ctypes.byref(cb), s_ptr, _dev(q, "q"), _dt(q), _dev(codes, "codes", torch.uint8),
+                                   _dev(norms, "norms", torch.float32), _dev(vcodes, "vcodes", torch.uint8),
+                                   _dev(vnorms, "vnorms", torch.float32), B, Hq, Hkv, T_cap,
+                                   _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
+                                   _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
     return out
 
 

@@ -228,3 +228,25 @@ def test_select_signs_validation_and_workspace(K):
     K._check(lib.kvq_codebook_pq(64, 8, 256, 2, P(FAKE), ctypes.byref(pq)))
     assert call(cbx=pq) == K.KVQ_ERR_UNSUPPORTED
     assert best.value == -7  # nothing written on failure
+
+
+def test_decode_qv_validation(K):
+    P = ctypes.c_void_p
+    cb = K.kvq_build_codebook(64, 4)
+    s = np.ones(64, dtype=np.int8)
+    lib = K._lib
+
+    def call(cbx=cb, vcodes=FAKE, vnorms=FAKE, odt=1, n_splits=0, T_cap=64):
+        return lib.kvq_decode_attn_qv(ctypes.byref(cbx), s.ctypes.data_as(P), P(FAKE), 1, P(FAKE), P(FAKE),
+                                      None if vcodes is None else P(vcodes), None if vnorms is None else P(vnorms),
+                                      1, 4, 2, T_cap, None, 0.125, P(FAKE), odt, None, 0, n_splits, None)
+    assert call(vcodes=None) == K.KVQ_ERR_INVALID_ARG
+    assert "vcodes" in K.kvq_last_error()
+    assert call(vnorms=None) == K.KVQ_ERR_INVALID_ARG
+    assert call(vnorms=FAKE + 4) == K.KVQ_ERR_INVALID_ARG
+    assert call(odt=4) == K.KVQ_ERR_INVALID_ARG
+    assert call(n_splits=-2) == K.KVQ_ERR_INVALID_ARG
+    assert call(T_cap=4096, n_splits=8) == K.KVQ_ERR_WORKSPACE
+    pq = K.kvq_codebook()
+    K._check(lib.kvq_codebook_pq(64, 8, 256, 2, P(FAKE), ctypes.byref(pq)))
+    assert call(cbx=pq) == K.KVQ_ERR_UNSUPPORTED
