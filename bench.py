@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # passes, scaled by a plain copy of known size).  It is reported only while the library sources hash to
 # the digest recorded with the counters; after any change to them the figure is stale and traffic is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_longctx_hbm_traffic.txt")
+TRAFFIC_FILE_QV = os.path.join(ROOT, "profiles", "qv_decode_kernel_longctx_hbm_traffic.txt")
 
 
 def library_source_digest():
@@ -50,12 +51,12 @@ def library_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic():
+def measured_traffic(path=TRAFFIC_FILE):
     """HBM bytes per launch from the committed counter summary, or None if absent or stale."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             if ":" in line:
                 k, v = line.split(":", 1)
@@ -105,6 +106,32 @@ def cpu_baseline(shape, signs, q, min_seconds=5.0):
     return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
             "sample": "the full decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode of the new "
                       "keys + decode attention, one thread, %.1f s" % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+
+
+def cpu_baseline_qv(shape, signs, q, min_seconds=5.0):
+    """Time the fp64 oracle (one thread) on the quantized-value decode step, repeated until min_seconds pass."""
+    import oracle
+    import workloads as W
+
+    lv, th = oracle.codebook(shape.d, shape.b)
+    scale = 1.0 / math.sqrt(shape.d)
+    cache = []
+    for bi in range(shape.B):  # keys and values encoded by the oracle itself, untimed
+        codes, norms, _, _ = oracle.encode_keys(th, signs, W.keys(shape, batches=[bi]), shape.b)
+        vcodes, vnorms, _, _ = oracle.encode_keys(th, signs, W.values(shape, batches=[bi]), shape.b)
+        cache.append((codes, norms, vcodes, vnorms))
+    done_keys, elapsed, passes = 0, 0.0, 0
+    while elapsed < min_seconds or passes == 0:
+        t0 = time.perf_counter()
+        for bi, (codes, norms, vcodes, vnorms) in enumerate(cache):
+            oracle.decode_attn_qv(lv, signs, q[bi:bi + 1], codes, norms, vcodes, vnorms, scale)
+        elapsed += time.perf_counter() - t0
+        done_keys += shape.B * shape.Hq * shape.T
+        passes += 1
+    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": "the full quantized-value decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle "
+                      "(value dequantization + decode attention), one thread, %.1f s"
+                      % (shape.B, shape.Hq, shape.T, passes, elapsed)}
 
 
 def run_suite(K, torch, reps=5, calls=30):
@@ -217,7 +244,26 @@ def run_suite(K, torch, reps=5, calls=30):
             K.kvq_encode_keys(cb, signs, keys, c, n)
 
         row(name, "encode", timed(enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
-        del caches, keys, scores
+
+        # values stored with the same codec (rotated-domain AV, one inverse transform per head)
+        vcs = []
+        for r in range(n_rot):
+            if r == 0:
+                vc0 = torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev)
+                vn0 = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                K.kvq_encode_keys(cb, signs, caches[0][2], vc0, vn0)
+                vcs.append((vc0, vn0))
+            else:
+                vcs.append((vcs[0][0].clone(), vcs[0][1].clone()))
+
+        def dec_qv(i):
+            c, n, _ = caches[i % n_rot]
+            vc, vn = vcs[i % n_rot]
+            K.kvq_decode_attn_qv(cb, signs, q, c, n, vc, vn, out=out, workspace=ws)
+
+        row(name, "decode-qv", timed(dec_qv, n_rot), B * Hkv * T * 2 * (bpk + 4) + B * Hq * d * 2, B * Hq * T,
+            B * Hkv * T)
+        del caches, keys, scores, vcs
         torch.cuda.empty_cache()
 
     # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes
@@ -295,6 +341,9 @@ def main(argv=None):
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline step, time every workload and operation (table on stderr)")
+    ap.add_argument("--variant", choices=("append", "qv"), default="append",
+                    help="append: the fused append + decode step over fp16 V (default); qv: decode attention "
+                         "with the values stored as codes of the same codec (kvq_decode_attn_qv)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -335,7 +384,16 @@ def main(argv=None):
     norms0 = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
     K.kvq_encode_keys(cb, signs, keys, codes0, norms0)
     del keys
-    caches = [(codes0, norms0, v0)] + [(codes0.clone(), norms0.clone(), v0.clone()) for _ in range(a.caches - 1)]
+    qv = a.variant == "qv"
+    if qv:  # the values go through the same encode; the fp16 values are not kept
+        vcodes0 = torch.empty_like(codes0)
+        vnorms0 = torch.empty_like(norms0)
+        K.kvq_encode_keys(cb, signs, v0, vcodes0, vnorms0)
+        del v0
+        caches = [(codes0, norms0, vcodes0, vnorms0)] + [
+            (codes0.clone(), norms0.clone(), vcodes0.clone(), vnorms0.clone()) for _ in range(a.caches - 1)]
+    else:
+        caches = [(codes0, norms0, v0)] + [(codes0.clone(), norms0.clone(), v0.clone()) for _ in range(a.caches - 1)]
     out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
     ws_bytes = K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, a.splits)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)  # split-merge counters start at zero
@@ -344,6 +402,10 @@ def main(argv=None):
     newk3 = newk[:, :, 0, :].contiguous()  # [B][Hkv][d]: the token appended on this step
 
     def step(i):
+        if qv:
+            c, n, vc, vn = caches[i % len(caches)]
+            K.kvq_decode_attn_qv(cb, signs, q, c, n, vc, vn, out=out, workspace=ws, n_splits=a.splits)
+            return
         c, n, v = caches[i % len(caches)]
         K.kvq_decode_attn_append(cb, signs, newk3, q, c, n, v, out=out, workspace=ws, n_splits=a.splits)
 
@@ -395,7 +457,8 @@ def main(argv=None):
 
     key_scores = B * Hq * T
     value = key_scores / (ms_per_step * 1e-3)
-    alg_bytes = algorithmic_bytes(shape, bpk, append=True)
+    # quantized values: key and value codes + norms of every cached key, and q
+    alg_bytes = (B * Hkv * T * 2 * (bpk + 4) + B * Hq * d * 2) if qv else algorithmic_bytes(shape, bpk, append=True)
     achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
     splits_used = ws_bytes // (B * Hq * (d + 4) * 4) if ws_bytes else 1
     eprint("step %.4f ms (one fused append + decode-attention launch)  -> %.4g key-scores/s" % (ms_per_step, value))
@@ -405,7 +468,7 @@ def main(argv=None):
     cpu = None
     if not a.no_cpu_baseline:
         eprint("timing the CPU oracle on a bounded sample (~%.0f s)" % a.cpu_seconds)
-        cpu = cpu_baseline(shape, signs, q_np, a.cpu_seconds)
+        cpu = (cpu_baseline_qv if qv else cpu_baseline)(shape, signs, q_np, a.cpu_seconds)
         eprint("cpu oracle: %.4g key-scores/s (%s)" % (cpu["value"], cpu["sample"]))
 
     rec = {
@@ -431,6 +494,14 @@ def main(argv=None):
                      "avg_launch_ms": attn_avg_ms, "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,
     }
+    if qv:
+        rec["config"].update({"workload": "longctx decode, values as 4-bit codes: B=8 Hq=32 Hkv=4 d=64 b=4 T=32768",
+                              "v_dtype": "codes",
+                              "step": "one kvq_decode_attn_qv launch: decode attention over T keys and values "
+                                      "stored as codes + norms"})
+        rec["roofline"].update({"traffic": measured_traffic(TRAFFIC_FILE_QV),
+                                "kernel": "qv_decode_kernel (MFMA scores from key levels + online softmax + "
+                                          "rotated-domain AV from value levels + split merge + inverse transform)"})
     print(json.dumps(rec), flush=True)
     return 0
 

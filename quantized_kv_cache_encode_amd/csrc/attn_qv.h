@@ -20,8 +20,9 @@
 //   the score accumulator of lane (r16, kq) holds keys 4kq..4kq+3 of head r16 & 7, which is exactly the
 //   B operand layout of the AV product, so the probabilities never leave registers;
 //   AV on the matrix cores: out'^T[coord][head] += V_hat^T[coord][key] . P^T[key][head]; lane (r16, kq)
-//   of the A operand holds coordinate r16 * D/16 + j of keys 4kq..4kq+3, whose codes are gathered from
-//   the four keys' code bytes by byte permutes, looked up, and scaled by the value norms (packed fp16).
+//   of the A operand holds coordinate r16 * D/16 + j of keys 4kq..4kq+3: every key's levels for two
+//   consecutive coordinates come from one read of a small LDS table indexed by the two codes, a byte
+//   permute transposes them, and the value norms scale them (packed fp16).
 // The online softmax, the wave merge and the split merge are those of the other decode kernel; the merged
 // rotated-domain output goes through an in-register fast Walsh-Hadamard transform and the sign flip.
 #pragma once
@@ -46,6 +47,11 @@ struct QvCfg {
   static constexpr bool kFastV = BITS != 3 && FV % 8 == 0;
   // rows that are not whole 32-bit words (d = 16 with b = 1 or 3: 2 or 6 bytes) are read in 16-bit units
   static constexpr bool kHalfRows = BPK % 4 != 0;
+  // key side with two codes per table entry: the entry [hi, hi, lo, lo] is the A operand itself, against a
+  // B operand that repeats the two coordinates (more B registers: not for d = 256)
+  static constexpr bool kKEntry = D <= 128;
+  // value side from the pair table (two coordinates per lane at least)
+  static constexpr bool kVPairs = DPL >= 2;
 };
 
 // A field of F bits that starts at a multiple of F bits in a code row, loaded into NF 32-bit words (the
@@ -167,22 +173,30 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t a0, uint32_t a1, uint32
   return __builtin_amdgcn_perm(x23, x01, 0x05040100u);
 }
 
-// Key-level table in LDS: entry e holds the levels of NC consecutive codes (code c = bits [c*BITS,
-// (c+1)*BITS) of e) as NC fp16 high parts followed by NC fp16 low parts (level - high part), so the read of
-// one entry yields both parts of that many A-operand values.
+// Level tables in LDS, indexed by two consecutive codes of one row (e = c0 | c1 << BITS):
+//   key table, entry e = [hi(c0), hi(c1)] [lo(c0), lo(c1)] (two words: fp16 high parts, then the fp16 low
+//   parts level - high part);
+//   value table, entry e = [lvl(c0), lvl(c1)] (one word, fp16).
+// Lookups are random, so the tables are stored 32 times over, one copy per LDS bank: word k of entry e of
+// copy c sits at byte e * 256 + k * 128 + c * 4 (each entry spans 256 bytes; the value table uses the first
+// half of each), and lane l reads copy l % 32, so the 32 lanes an LDS cycle serves never meet in a bank.
+// With 4-bit codes the index is a whole byte of the code row, and one byte permute forms the address
+// index * 256 + copy * 4 (+ the value table's base, 2^16) from the code word and the lane's copy offset.
 template <int BITS>
-struct KTab {
-  static constexpr int NC = BITS <= 2 ? 4 : 2;  // codes per entry
-  static constexpr int IB = NC * BITS;          // index bits
-  static constexpr int NE = 1 << IB;            // entries
-  static constexpr int ES = NC * 4;             // bytes per entry
+struct LvlTabs {
+  static constexpr int IB = 2 * BITS;                  // index bits
+  static constexpr int NE = 1 << IB;                   // entries
+  static constexpr size_t v_off = (size_t)NE * 256;    // key table first (2^16 bytes for 4-bit codes)
+  static constexpr size_t bytes = 2 * v_off;
+  static constexpr bool kPermAddr = BITS == 4;
 };
 
 template <class C, int GG>
 struct QvPlan {
   static constexpr size_t red_bytes = (size_t)kWaves * GG * (C::D + 2) * 4;
-  static constexpr size_t ktab_bytes = (size_t)KTab<C::BITS>::NE * KTab<C::BITS>::ES;
-  static constexpr size_t region0 = ((red_bytes > ktab_bytes ? red_bytes : ktab_bytes) + 15) / 16 * 16;
+  static constexpr size_t vtab_off = LvlTabs<C::BITS>::v_off;
+  static constexpr size_t tabs_bytes = LvlTabs<C::BITS>::bytes;
+  static constexpr size_t region0 = ((red_bytes > tabs_bytes ? red_bytes : tabs_bytes) + 15) / 16 * 16;
   static constexpr size_t consts_off = region0;                     // 16 levels, merge flag (+96)
   static constexpr size_t qs_off = consts_off + 128;                // GG * D floats (rotated queries)
   static constexpr size_t xs_off = qs_off + (size_t)GG * C::D * 4;  // GG * D floats (merged output)
@@ -280,35 +294,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     tab.lo[k] = lo;
     tab.hi[k] = hi;
   }
-  // key-level table (the table region is free until the wave merge)
-  using KT = KTab<BITS>;
-  for (int e = tid; e < KT::NE; e += kThreads) {
-    _Float16 hl[2 * KT::NC];
+  // level tables (the table region is free until the wave merge): every thread makes one word of one
+  // entry and writes its 32 copies (128 contiguous bytes)
+  using LT = LvlTabs<BITS>;
+  unsigned char* vtab = smem + Plan::vtab_off;
+  {
+    typedef unsigned u4w __attribute__((ext_vector_type(4)));
+    // the 8 stores of a lane start at different 16-byte quarters of its run, so that the lanes of one store
+    // spread over all banks (runs are 128 bytes apart, i.e. in the same banks)
+    auto put32 = [&](unsigned char* dst, uint32_t w) {
 #pragma unroll
-    for (int cc2 = 0; cc2 < KT::NC; ++cc2) {
-      const float x = lv[(e >> (cc2 * BITS)) & ((1 << BITS) - 1)];
-      const _Float16 h = (_Float16)x;
-      hl[cc2] = h;
-      hl[KT::NC + cc2] = (_Float16)(x - (float)h);
+      for (int k = 0; k < 8; ++k) *reinterpret_cast<u4w*>(dst + 16 * ((k + lane) & 7)) = u4w{w, w, w, w};
+    };
+    auto pack2 = [](_Float16 a, _Float16 b) -> uint32_t {
+      return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    };
+    for (int x = tid; x < LT::NE * 2; x += kThreads) {  // key table: x = entry * 2 + part
+      const int e = x >> 1, part = x & 1;                  // part 0: high parts, 1: low parts
+      const float l0 = lv[e & ((1 << BITS) - 1)], l1 = lv[e >> BITS];
+      const _Float16 h0 = (_Float16)l0, h1 = (_Float16)l1;
+      const uint32_t w = part ? pack2((_Float16)(l0 - (float)h0), (_Float16)(l1 - (float)h1)) : pack2(h0, h1);
+      put32(smem + (size_t)x * 128, w);
     }
-    if constexpr (KT::NC == 4) {
-      typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-      *reinterpret_cast<h8*>(smem + (size_t)e * KT::ES) = h8{hl[0], hl[1], hl[2], hl[3], hl[4], hl[5], hl[6], hl[7]};
-    } else {
-      *reinterpret_cast<half4_t*>(smem + (size_t)e * KT::ES) = half4_t{hl[0], hl[1], hl[2], hl[3]};
+    if constexpr (C::kVPairs) {
+      for (int e = tid; e < LT::NE; e += kThreads)
+        put32(vtab + (size_t)e * 256, pack2((_Float16)lv[e & ((1 << BITS) - 1)], (_Float16)lv[e >> BITS]));
     }
   }
-  // B operands of the score products: column r16 holds head r16 & 7, high part (r16 < 8) or low part
-  half4_t bq[KB];
+  const uint32_t bank4 = (uint32_t)(lane & 31) * 4;  // this lane's copy
+  const uint32_t bank4v = bank4 | (uint32_t)Plan::vtab_off;
+  // byte address of entry idx: idx * 256 + base, idx the IB bits at bit `bit` of a field
+  auto ent_addr = [&](const auto& f, int bit, uint32_t base) -> uint32_t {
+    if constexpr (LT::kPermAddr) {
+      // [base.b0, code byte, base.b2, 0] (base < 2^24 with a zero second byte)
+      const int w = bit / 32, m = (bit % 32) / 8;
+      return __builtin_amdgcn_perm(f[w], base, 0x0c020400u | ((uint32_t)(4 + m) << 8));
+    } else {
+      return base + field_bits<LT::IB, sizeof(f) / 4>(f, bit) * 256u;
+    }
+  };
+  // B operands of the score products: column r16 holds head r16 & 7, high part (r16 < 8) or low part.
+  // Slot m of product kb holds the coordinate of code slot_code(kb, m) of this lane's quarter row.
+  constexpr int NBQ = C::kKEntry ? D / 8 : KB;
+  half4_t bq[NBQ];
   {
     const int g = r16 & 7;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < NBQ; ++kb) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        const int code = C::kKEntry ? 2 * kb + (m & 1) : 4 * kb + m;
         _Float16 v = 0;
         if (g < GG) {
-          const float x = qs[g * D + kq * (D / 4) + 4 * kb + m];
+          const float x = qs[g * D + kq * (D / 4) + code];
           const _Float16 h = (_Float16)x;
           v = r16 < 8 ? h : (_Float16)(x - (float)h);
         }
@@ -329,36 +367,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     float z[TPC][4];
 #pragma unroll
     for (int t = 0; t < TPC; ++t) {
-      // A operands: levels of codes 4kb .. 4kb+3 of this lane's quarter row, high and low parts
+      // A operands: levels of this lane's quarter row from the key table, high and low parts
       float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+      typedef unsigned u2 __attribute__((ext_vector_type(2)));
+      auto kent = [&](uint32_t addr) -> u2 {
+        const unsigned char* a = smem + addr;
+        return u2{*reinterpret_cast<const uint32_t*>(a), *reinterpret_cast<const uint32_t*>(a + 128)};
+      };
+      if constexpr (C::kKEntry) {
+        // one entry = [hi(c), hi(c')] [lo(c), lo(c')] of codes 2e, 2e+1: a whole operand
 #pragma unroll
-      for (int kb2 = 0; kb2 < KB; ++kb2) {
-        half4_t ahi, alo;
-        if constexpr (KT::NC == 4) {
-          const uint32_t idx = field_bits<KT::IB, NFK>(k.kc[t], 4 * kb2 * BITS);
-          typedef unsigned u4 __attribute__((ext_vector_type(4)));
-          const u4 e = *reinterpret_cast<const u4*>(smem + idx * KT::ES);
-          typedef unsigned u2 __attribute__((ext_vector_type(2)));
-          ahi = __builtin_bit_cast(half4_t, u2{e[0], e[1]});
-          alo = __builtin_bit_cast(half4_t, u2{e[2], e[3]});
-        } else {
-          const uint32_t i0 = field_bits<KT::IB, NFK>(k.kc[t], 4 * kb2 * BITS);
-          const uint32_t i1 = field_bits<KT::IB, NFK>(k.kc[t], (4 * kb2 + 2) * BITS);
-          typedef unsigned u2 __attribute__((ext_vector_type(2)));
-          const u2 e0 = *reinterpret_cast<const u2*>(smem + i0 * KT::ES);
-          const u2 e1 = *reinterpret_cast<const u2*>(smem + i1 * KT::ES);
-          ahi = __builtin_bit_cast(half4_t, u2{e0[0], e1[0]});
-          alo = __builtin_bit_cast(half4_t, u2{e0[1], e1[1]});
+        for (int e2 = 0; e2 < D / 8; ++e2) {
+          const u2 ent = kent(ent_addr(k.kc[t], 2 * e2 * BITS, bank4));
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, ent), bq[e2], acc, 0, 0, 0);
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bq[kb2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bq[kb2], acc, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int kb2 = 0; kb2 < KB; ++kb2) {
+          const u2 e0 = kent(ent_addr(k.kc[t], 4 * kb2 * BITS, bank4));
+          const u2 e1 = kent(ent_addr(k.kc[t], (4 * kb2 + 2) * BITS, bank4));
+          const half4_t ahi = __builtin_bit_cast(half4_t, u2{e0[0], e1[0]});
+          const half4_t alo = __builtin_bit_cast(half4_t, u2{e0[1], e1[1]});
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi, bq[kb2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(alo, bq[kb2], acc, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float s = acc[i] + dpp_f<0x128>(acc[i]);  // row_ror:8 -- high part + low part
-        const bool valid = cc + 16 * t + 4 * kq + i < n_valid;
-        z[t][i] = valid ? s * (k.kn[t][i] * p.zscale) : -INFINITY;
+        z[t][i] = s * (k.kn[t][i] * p.zscale);
       }
+    }
+    if (cc + C::CH > n_valid) {  // the split's last, partial chunk
+#pragma unroll
+      for (int t = 0; t < TPC; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[t][i] = cc + 16 * t + 4 * kq + i < n_valid ? z[t][i] : -INFINITY;
     }
     // ---- online softmax with the lazily raised maximum (probabilities stay <= 2^8)
     float zmax = z[0][0];
@@ -389,22 +433,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
       const half2_t n01 = half2_t{(_Float16)k.vn[t][0], (_Float16)k.vn[t][1]};
       const half2_t n23 = half2_t{(_Float16)k.vn[t][2], (_Float16)k.vn[t][3]};
+      if constexpr (C::kVPairs) {
+        // coordinates 2pm and 2pm+1 of each of the four keys from the pair table, then a 2 x 4 transpose
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) {
-        uint32_t sel;
-        if constexpr (C::kFastV) {
-          const int bit = j * BITS, m = bit / 8, wi = m / 4;
-          const uint32_t g = gather_byte(k.vc[t][0][wi], k.vc[t][1][wi], k.vc[t][2][wi], k.vc[t][3][wi], m % 4);
-          sel = (g >> (bit % 8)) & C::MB;
-        } else {
-          sel = field_code<BITS, NFV>(k.vc[t][0], j) | (field_code<BITS, NFV>(k.vc[t][1], j) << 8) |
-                (field_code<BITS, NFV>(k.vc[t][2], j) << 16) | (field_code<BITS, NFV>(k.vc[t][3], j) << 24);
+        for (int pm = 0; pm < DPL / 2; ++pm) {
+          uint32_t e[4];
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            e[s2] = *reinterpret_cast<const uint32_t*>(smem + ent_addr(k.vc[t][s2], 2 * pm * BITS, bank4v));
+          typedef unsigned u2 __attribute__((ext_vector_type(2)));
+          const half4_t lo4 = __builtin_bit_cast(half4_t, u2{__builtin_amdgcn_perm(e[1], e[0], 0x05040100u),
+                                                             __builtin_amdgcn_perm(e[3], e[2], 0x05040100u)});
+          const half4_t hi4 = __builtin_bit_cast(half4_t, u2{__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                                                             __builtin_amdgcn_perm(e[3], e[2], 0x07060302u)});
+          const half2_t a01 = half2_t{lo4[0], lo4[1]} * n01, a23 = half2_t{lo4[2], lo4[3]} * n23;
+          const half2_t b01 = half2_t{hi4[0], hi4[1]} * n01, b23 = half2_t{hi4[2], hi4[3]} * n23;
+          oacc[2 * pm] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_t{a01[0], a01[1], a23[0], a23[1]}, pb,
+                                                               oacc[2 * pm], 0, 0, 0);
+          oacc[2 * pm + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(half4_t{b01[0], b01[1], b23[0], b23[1]}, pb,
+                                                                   oacc[2 * pm + 1], 0, 0, 0);
         }
-        const half4_t lvl = lookup4<BITS>(sel, tab);
-        const half2_t v01 = half2_t{lvl[0], lvl[1]} * n01;
-        const half2_t v23 = half2_t{lvl[2], lvl[3]} * n23;
-        const half4_t av = half4_t{v01[0], v01[1], v23[0], v23[1]};
-        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, oacc[j], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) {
+          uint32_t sel;
+          if constexpr (C::kFastV) {
+            const int bit = j * BITS, m = bit / 8, wi = m / 4;
+            const uint32_t g = gather_byte(k.vc[t][0][wi], k.vc[t][1][wi], k.vc[t][2][wi], k.vc[t][3][wi], m % 4);
+            sel = (g >> (bit % 8)) & C::MB;
+          } else {
+            sel = field_code<BITS, NFV>(k.vc[t][0], j) | (field_code<BITS, NFV>(k.vc[t][1], j) << 8) |
+                  (field_code<BITS, NFV>(k.vc[t][2], j) << 16) | (field_code<BITS, NFV>(k.vc[t][3], j) << 24);
+          }
+          const half4_t lvl = lookup4<BITS>(sel, tab);
+          const half2_t v01 = half2_t{lvl[0], lvl[1]} * n01;
+          const half2_t v23 = half2_t{lvl[2], lvl[3]} * n23;
+          const half4_t av = half4_t{v01[0], v01[1], v23[0], v23[1]};
+          oacc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, oacc[j], 0, 0, 0);
+        }
       }
     }
   };
