@@ -72,16 +72,20 @@ struct HlmScorer {
   static constexpr bool kRotate = true;
   static constexpr bool kNorm = true;
   static constexpr bool kNibbles = BITS == 4;  // two codes per byte: byte-wise address extraction
+  static constexpr bool kIntLut = true;        // fixed-point table entries, summed exactly in 32-bit integers
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) { return code_at<BITS, NW>(w, i); }
-  // LUT[g][i][j] = q'_{g,i} * c_j with q' = H D q / sqrt(d) held in qs; one HW-wide entry (HW heads) per
-  // (head group, coordinate, level).
+  // LUT[g][i][j] = q'_{g,i} * c_j with q' = H D q / sqrt(d) held in qs, as the integer nearest to
+  // q'_{g,i} * c_j * 2^e_g (fix_exp: the table of head g sums to at most 2^30 in magnitude, so integer sums
+  // of one entry per row never overflow); one HW-wide entry (HW heads) per (head group, coordinate, level).
   // Each work item fills JPT consecutive levels of one (head group, coordinate) row.
   template <int GG, int HW>
-  __device__ static void build(const AttnParams&, const float* qs, const float* lv, float* lut, int, int tid) {
-    using E = typename VecF<HW>::type;
+  __device__ static void build(const AttnParams&, const float* qs, const float* qa, const float* lv, float* lut,
+                               int, int tid) {
+    using E = typename VecI<HW>::type;
     constexpr int JPT = COLS < 4 ? COLS : 4;
     constexpr int NJ = COLS / JPT;
     constexpr int total = (GG / HW) * ROWS * NJ;
+    const float cmax = fmaxf(fabsf(lv[0]), fabsf(lv[COLS - 1]));
     E* L = reinterpret_cast<E*>(lut);
     for (int e = tid; e < total; e += kThreads) {
       const int j0 = (e % NJ) * JPT;
@@ -89,14 +93,17 @@ struct HlmScorer {
       const int g0 = (e / (NJ * ROWS)) * HW;
       float qv[HW];
 #pragma unroll
-      for (int h = 0; h < HW; ++h) qv[h] = qs[(g0 + h) * D + i];
+      for (int h = 0; h < HW; ++h) qv[h] = qs[(g0 + h) * D + i] * pow2f(fix_exp(qa[g0 + h], cmax));
       E* row = L + (size_t)(e / NJ) * COLS + j0;
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
         const float c = lv[j0 + jj];
-        if constexpr (HW == 4) row[jj] = make_float4(qv[0] * c, qv[1] * c, qv[2] * c, qv[3] * c);
-        else if constexpr (HW == 2) row[jj] = make_float2(qv[0] * c, qv[1] * c);
-        else row[jj] = qv[0] * c;
+        int x[HW];
+#pragma unroll
+        for (int h = 0; h < HW; ++h) x[h] = (int)__builtin_rintf(qv[h] * c);
+        if constexpr (HW == 4) row[jj] = make_int4(x[0], x[1], x[2], x[3]);
+        else if constexpr (HW == 2) row[jj] = make_int2(x[0], x[1]);
+        else row[jj] = x[0];
       }
     }
   }
@@ -115,12 +122,14 @@ struct PqScorer {
   static constexpr bool kRotate = false;
   static constexpr bool kNorm = false;
   static constexpr bool kNibbles = false;
+  static constexpr bool kIntLut = false;
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) {
     return (w[i >> 2] >> (8 * (i & 3))) & 255u;
   }
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).
   template <int GG, int HW>
-  __device__ static void build(const AttnParams& p, const float* qs, const float*, float* lut, int kvh, int tid) {
+  __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
+                               int tid) {
     constexpr int total = GG * ROWS * COLS;
     const int K = p.pq_K;
     const float* cent = p.pq_cent + (size_t)kvh * M * K * DS;
@@ -152,7 +161,8 @@ struct LdsPlan {
   static constexpr size_t newcode_off = consts_off + 160;
   static constexpr size_t newnorm_off = consts_off + 288;
   static constexpr size_t qs_off = consts_off + 304;              // GG * D floats
-  static constexpr size_t pst_off = qs_off + (size_t)GG * S::D * 4;
+  static constexpr size_t qa_off = qs_off + (size_t)GG * S::D * 4;  // GG floats: sum_i |q'_{g,i}|
+  static constexpr size_t pst_off = qa_off + 32;
   static constexpr size_t pst_bytes(bool f16) { return (size_t)kWaves * GG * kChunk * (f16 ? 2 : 4); }
   static constexpr size_t total(bool f16) { return pst_off + pst_bytes(f16); }
 };
@@ -184,7 +194,7 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
 template <class S, int GG, class F>
-__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* lv, int tid, F&& between) {
+__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
   if (tid < 16) lv[tid] = p.levels[tid];
   if constexpr (S::kRotate) {
@@ -244,6 +254,14 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* l
       const float rs = 1.0f / __builtin_sqrtf((float)D);
 #pragma unroll
       for (int t = 0; t < 8; ++t) qs[g * D + 8 * k + t] = x[t] * rs;
+      if (qa != nullptr) {  // sum_i |q'_i| of the query: the bound that scales its fixed-point table
+        float a = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a += fabsf(x[t]);
+#pragma unroll
+        for (int dl = 1; dl < LPQ; dl <<= 1) a += __shfl_xor(a, dl, 64);
+        if (k == 0) qa[g] = a * rs;
+      }
     }
   } else {
     between();
@@ -255,8 +273,12 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* l
   lds_barrier();
 }
 
-// Scores of the key held by this lane for all GG heads (before the norm).
-// `lut` is the byte address of the table in LDS.
+// Accumulator of a scorer's table sums: 32-bit integers for fixed-point tables, else fp32.
+template <class S>
+using ScoreAcc = typename std::conditional<S::kIntLut, uint32_t, float>::type;
+
+// Scores of the key held by this lane for all GG heads (before the norm; for fixed-point tables before the
+// head's scale 2^-e_g as well).  `lut` is the byte address of the table in LDS.
 //
 // Every coordinate i contributes the table entry at (row i, column code_i) for each head group; its LDS
 // byte offset within the row is code_i * ES.  The gathers run one stage (4 coordinates x NQ head groups)
@@ -265,13 +287,13 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* l
 // The first stage initialises the sums.
 template <class S, int GG>
 __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut, const uint32_t (&w)[S::NW],
-                                           float (&acc)[GG]) {
+                                           ScoreAcc<S> (&acc)[GG]) {
   constexpr int HW = GG < 4 ? GG : 4;
   constexpr int NQ = GG / HW;
   constexpr int ES = HW * 4;  // bytes per table entry
   constexpr int LG = ES == 16 ? 4 : (ES == 8 ? 3 : 2);
   constexpr uint32_t NMASK = 0xFu << LG;
-  using E = typename VecF<HW>::type;
+  using E = typename std::conditional<S::kIntLut, typename VecI<HW>::type, typename VecF<HW>::type>::type;
   constexpr int ST = 4;  // coordinates per stage
   static_assert(S::ROWS % ST == 0, "rows come in stages of four");
   constexpr int NST = S::ROWS / ST;
@@ -464,6 +486,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   float* s_newn = reinterpret_cast<float*>(smem + Plan::newnorm_off);
   static_assert(S::NW * 4 <= 128, "appended key's codes fit their LDS slot");
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
+  float* qa = reinterpret_cast<float*>(smem + Plan::qa_off);
   PT* pst = reinterpret_cast<PT*>(smem + Plan::pst_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -542,7 +565,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
   // burst streams in while the queries are rotated and the table is built.
-  prologue<S, GG>(p, u, qs, lv, tid, [&] {
+  prologue<S, GG>(p, u, qs, qa, lv, tid, [&] {
     fetch_codes(c, ka);
     fetch_v(c, ka);
     const int ko = lane * 8 * kesz;
@@ -571,9 +594,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     }
   }
-  S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  S::template build<GG, HW>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   if (lane == 0) s_prog[wid] = 0;
   lds_barrier();
+  // softmax argument of head g per unit of table sum and of key norm: scale * log2(e) (* 2^-e_g)
+  float hz[GG];
+#pragma unroll
+  for (int g = 0; g < GG; ++g) {
+    hz[g] = p.zscale;
+    if constexpr (S::kIntLut) hz[g] *= pow2f(-fix_exp(qa[g], fmaxf(fabsf(lv[0]), fabsf(lv[S::COLS - 1]))));
+  }
 
   float m_run[GG], l_lane[GG];
 #pragma unroll
@@ -602,12 +632,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       for (int ks = 0; ks < 4; ++ks) load_v(cc, ks, vc[ks]);
     }
     // ---- scores from the table
-    float acc[GG];
+    ScoreAcc<S> acc[GG];
     lut_scores<S, GG>(smem, k.w, acc);
     float z[GG];
-    const float zs = S::kNorm ? k.nrm * p.zscale : p.zscale;
 #pragma unroll
-    for (int g = 0; g < GG; ++g) z[g] = acc[g] * zs;
+    for (int g = 0; g < GG; ++g) {
+      if constexpr (S::kIntLut) z[g] = (float)(int)acc[g] * (k.nrm * hz[g]);
+      else z[g] = acc[g] * (S::kNorm ? k.nrm * hz[g] : hz[g]);
+    }
     if (cc + kChunk > n_valid) {  // the split's last, partial chunk
       const bool valid = cc + lane < n_valid;
 #pragma unroll
@@ -798,6 +830,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   __shared__ __align__(16) unsigned char smem[Plan::pst_off];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
+  float* qa = reinterpret_cast<float*>(smem + Plan::qa_off);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -825,8 +858,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // and stores at or past T_cap are dropped by the bounds check
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.scores + ((size_t)u.b * p.Hq + u.h0) * p.T_cap,
                                               (int64_t)GG * p.T_cap * 4);
+  float hs[GG];  // score per unit of table sum: 2^-e_g for fixed-point tables
   auto score = [&](int cc, const uint32_t (&w)[S::NW], float n) {
-    float acc[GG];
+    ScoreAcc<S> acc[GG];
     lut_scores<S, GG>(smem, w, acc);
     const int t = cc + lane;
     const bool valid = t < n_valid;
@@ -834,15 +868,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     const int voff = t < n_stop ? (int)(t_begin + t) * 4 : 0x40000000;
 #pragma unroll
     for (int g = 0; g < GG; ++g) {
-      const float sc = S::kNorm ? n * acc[g] : acc[g];
+      const float sc = S::kIntLut ? n * ((float)(int)acc[g] * hs[g]) : (S::kNorm ? n * acc[g] : acc[g]);
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, valid ? sc : -INFINITY), rs, voff,
                                             g * p.T_cap * 4, 0);
     }
   };
   int c = wid * kChunk;
-  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c, wa, na); });
-  S::template build<GG, HW>(p, qs, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  prologue<S, GG>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); });
+  S::template build<GG, HW>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   lds_barrier();
+#pragma unroll
+  for (int g = 0; g < GG; ++g)
+    hs[g] = S::kIntLut ? pow2f(-fix_exp(qa[g], fmaxf(fabsf(lv[0]), fabsf(lv[S::COLS - 1])))) : 1.0f;
 
   for (; c < n_stop; c += 2 * STR) {
     fetch(c + STR, wb, nb);

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   constexpr int STR = kWaves * C::CH;
   int c = wid * C::CH;
   Chunk ka, kb;
-  prologue<S, GG>(p, u, qs, lv, tid, [&] { fetch(c, ka); });
+  prologue<S, GG>(p, u, qs, nullptr, lv, tid, [&] { fetch(c, ka); });
 
   // fp16 level tables (from LDS, so they live in vector registers as the permutes need)
   LevelTab tab;

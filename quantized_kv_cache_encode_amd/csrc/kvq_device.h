@@ -17,6 +17,11 @@ template <> struct VecF<1> { typedef float type; };
 template <> struct VecF<2> { typedef float2 type; };
 template <> struct VecF<4> { typedef float4 type; };
 
+template <int N> struct VecI;
+template <> struct VecI<1> { typedef int type; };
+template <> struct VecI<2> { typedef int2 type; };
+template <> struct VecI<4> { typedef int4 type; };
+
 __device__ __forceinline__ void set_from(float* acc, float e) { acc[0] = e; }
 __device__ __forceinline__ void set_from(float* acc, float2 e) { acc[0] = e.x; acc[1] = e.y; }
 __device__ __forceinline__ void set_from(float* acc, float4 e) { acc[0] = e.x; acc[1] = e.y; acc[2] = e.z; acc[3] = e.w; }
@@ -24,6 +29,33 @@ __device__ __forceinline__ void add_into(float* acc, float e) { acc[0] += e; }
 __device__ __forceinline__ void add_into(float* acc, float2 e) { acc[0] += e.x; acc[1] += e.y; }
 __device__ __forceinline__ void add_into(float* acc, float4 e) {
   acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
+}
+
+// Integer sums of table entries wrap modulo 2^32 (unsigned); the tables are scaled so that they never do.
+__device__ __forceinline__ void set_from(uint32_t* acc, int e) { acc[0] = (uint32_t)e; }
+__device__ __forceinline__ void set_from(uint32_t* acc, int2 e) { acc[0] = (uint32_t)e.x; acc[1] = (uint32_t)e.y; }
+__device__ __forceinline__ void set_from(uint32_t* acc, int4 e) {
+  acc[0] = (uint32_t)e.x; acc[1] = (uint32_t)e.y; acc[2] = (uint32_t)e.z; acc[3] = (uint32_t)e.w;
+}
+__device__ __forceinline__ void add_into(uint32_t* acc, int e) { acc[0] += (uint32_t)e; }
+__device__ __forceinline__ void add_into(uint32_t* acc, int2 e) { acc[0] += (uint32_t)e.x; acc[1] += (uint32_t)e.y; }
+__device__ __forceinline__ void add_into(uint32_t* acc, int4 e) {
+  acc[0] += (uint32_t)e.x; acc[1] += (uint32_t)e.y; acc[2] += (uint32_t)e.z; acc[3] += (uint32_t)e.w;
+}
+
+// 2^e as a float, for -126 <= e <= 126 (exact).
+__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
+
+// Exponent of the fixed-point scale of one head's score table.  With A = sum_i |q'_i| and cmax the largest
+// level magnitude, any sum of one entry per coordinate is at most A * cmax in magnitude; the scale 2^e with
+// e = 29 - floor(log2(A * cmax)) keeps that below 2^30, and each entry's rounding error is at most 2^-(e+1)
+// <= A * cmax * 2^-30.  For A * cmax = 0 or below the normal range e is clamped to 126 (the entries are
+// then 0 or rounded to 0); for infinite or NaN A the table is meaningless, as the query is.
+__device__ __forceinline__ int fix_exp(float a, float cmax) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, a * cmax);
+  const int k = (int)((bits >> 23) & 0xffu) - 127;
+  const int e = 29 - k;
+  return e < -126 ? -126 : (e > 126 ? 126 : e);
 }
 
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it

@@ -163,6 +163,32 @@ def test_score_parity(K, oracle_mod, name, shape, batches, T, lens):
     log("  max |ds|/(|q||k|) = %.3g" % float(np.max(err / (tol[fin] / 1e-4 + 1e-30))))
 
 
+def test_score_heads_of_very_different_norms(K, oracle_mod):
+    """Each query head's table has its own fixed-point scale: heads whose norms span 1e-4 .. 1e4 (fp32
+    queries) and an all-zero head must each meet the per-head score bar; the zero head scores exactly 0."""
+    import torch
+    shape = W.scaled(W.LONGCTX, B=1, T=700)
+    case = make_hlm_case(shape)
+    q = case["q"].astype(np.float32)
+    hs = np.logspace(-4, 4, shape.Hq).astype(np.float32)
+    hs[5] = 0.0
+    q = q * hs[None, :, None]
+    ref_codes, ref_norms, _ = oracle_cache(oracle_mod, shape, case["keys"], case["signs"])
+    codes, norms = _upload_cache(ref_codes, ref_norms)
+    cb = K.kvq_build_codebook(shape.d, shape.b)
+    got = K.kvq_score(cb, case["signs"], torch_dev(q), codes, norms)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    lv, _ = oracle_mod.codebook(shape.d, shape.b)
+    ref = oracle_mod.scores(lv, case["signs"], q, ref_codes, ref_norms)
+    tol = score_tolerance(q, ref_norms, shape.Hq // shape.Hkv)
+    assert np.all(got[0, 5] == 0.0)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), "max excess %g" % float(np.max(err - tol))
+    ratio = err / np.maximum(tol / 1e-4, 1e-30)
+    log("  max |ds|/(|q||k|) over heads with norms 1e-4..1e4: %.3g" % float(ratio.max()))
+
+
 DECODE_CASES = [
     # name, shape, batches, T, seq_lens, n_splits, out dtype
     ("tiny", W.TINY, None, None, None, 0, "f32"),
