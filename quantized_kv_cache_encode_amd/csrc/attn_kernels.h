@@ -60,24 +60,31 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int i) {
   return x & ((1u << B) - 1u);
 }
 
-// Scorer for the Hadamard + Lloyd-Max codec: rows = coordinates, cols = levels.
+// Scorer for the Hadamard + Lloyd-Max codec.  A table row covers GRP consecutive coordinates whose codes
+// fill one 4-bit field of the packed row (GRP = 4 / b for b = 1, 2, 4; one coordinate for b = 3): its
+// column is that field, and entry (r, n) = sum_k q'_{r GRP + k} * c_{code_k(n)} with code_k(n) the k-th b-bit
+// part of n.  So every table lookup adds 4 bits' worth of codes, and a key takes d b / 4 lookups (d for
+// b = 3) however many coordinates a row spans.
 template <int D_, int BITS>
 struct HlmScorer {
   static constexpr int D = D_;
-  static constexpr int ROWS = D;
-  static constexpr int COLS = 1 << BITS;
+  static constexpr int LEVELS = 1 << BITS;
+  static constexpr int GRP = BITS == 3 ? 1 : 4 / BITS;  // coordinates per table row
+  static constexpr int ROWS = D / GRP;
+  static constexpr int COLS = 1 << (BITS * GRP);
   static constexpr int CODE_BITS = BITS;
   static constexpr int BPK = D * BITS / 8;
   static constexpr int NW = (BPK + 3) / 4;
   static constexpr bool kRotate = true;
   static constexpr bool kNorm = true;
-  static constexpr bool kNibbles = BITS == 4;  // two codes per byte: byte-wise address extraction
-  static constexpr bool kIntLut = true;        // fixed-point table entries, summed exactly in 32-bit integers
+  static constexpr bool kNibbles = BITS * GRP == 4;  // rows indexed by the 4-bit fields of the packed codes
+  static constexpr bool kIntLut = true;              // fixed-point table entries, summed exactly in 32-bit integers
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) { return code_at<BITS, NW>(w, i); }
-  // LUT[g][i][j] = q'_{g,i} * c_j with q' = H D q / sqrt(d) held in qs, as the integer nearest to
-  // q'_{g,i} * c_j * 2^e_g (fix_exp: the table of head g sums to at most 2^30 in magnitude, so integer sums
-  // of one entry per row never overflow); one HW-wide entry (HW heads) per (head group, coordinate, level).
-  // Each work item fills JPT consecutive levels of one (head group, coordinate) row.
+  __device__ static __forceinline__ float level_max(const float* lv) { return fmaxf(fabsf(lv[0]), fabsf(lv[LEVELS - 1])); }
+  // Table of head g, with q' = H D q / sqrt(d) held in qs: every entry is the integer nearest to its value
+  // times 2^e_g (fix_exp), so the table of head g sums to at most 2^30 in magnitude along any choice of one
+  // entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
+  // column); each work item fills JPT consecutive columns of one (head group, row).
   template <int GG, int HW>
   __device__ static void build(const AttnParams&, const float* qs, const float* qa, const float* lv, float* lut,
                                int, int tid) {
@@ -85,22 +92,31 @@ struct HlmScorer {
     constexpr int JPT = COLS < 4 ? COLS : 4;
     constexpr int NJ = COLS / JPT;
     constexpr int total = (GG / HW) * ROWS * NJ;
-    const float cmax = fmaxf(fabsf(lv[0]), fabsf(lv[COLS - 1]));
+    const float cmax = level_max(lv);
     E* L = reinterpret_cast<E*>(lut);
     for (int e = tid; e < total; e += kThreads) {
       const int j0 = (e % NJ) * JPT;
-      const int i = (e / NJ) % ROWS;
+      const int r = (e / NJ) % ROWS;
       const int g0 = (e / (NJ * ROWS)) * HW;
-      float qv[HW];
+      float qv[HW][GRP];
 #pragma unroll
-      for (int h = 0; h < HW; ++h) qv[h] = qs[(g0 + h) * D + i] * pow2f(fix_exp(qa[g0 + h], cmax));
+      for (int h = 0; h < HW; ++h) {
+        const float sc = pow2f(fix_exp(qa[g0 + h], cmax));
+#pragma unroll
+        for (int k = 0; k < GRP; ++k) qv[h][k] = qs[(g0 + h) * D + r * GRP + k] * sc;
+      }
       E* row = L + (size_t)(e / NJ) * COLS + j0;
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
-        const float c = lv[j0 + jj];
+        const int n = j0 + jj;
         int x[HW];
 #pragma unroll
-        for (int h = 0; h < HW; ++h) x[h] = (int)__builtin_rintf(qv[h] * c);
+        for (int h = 0; h < HW; ++h) {
+          float t = qv[h][0] * lv[n & (LEVELS - 1)];
+#pragma unroll
+          for (int k = 1; k < GRP; ++k) t += qv[h][k] * lv[(n >> (k * BITS)) & (LEVELS - 1)];
+          x[h] = (int)__builtin_rintf(t);
+        }
         if constexpr (HW == 4) row[jj] = make_int4(x[0], x[1], x[2], x[3]);
         else if constexpr (HW == 2) row[jj] = make_int2(x[0], x[1]);
         else row[jj] = x[0];
@@ -126,6 +142,7 @@ struct PqScorer {
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) {
     return (w[i >> 2] >> (8 * (i & 3))) & 255u;
   }
+  __device__ static __forceinline__ float level_max(const float*) { return 1.0f; }
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).
   template <int GG, int HW>
   __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
   for (int g = 0; g < GG; ++g) {
     hz[g] = p.zscale;
-    if constexpr (S::kIntLut) hz[g] *= pow2f(-fix_exp(qa[g], fmaxf(fabsf(lv[0]), fabsf(lv[S::COLS - 1]))));
+    if constexpr (S::kIntLut) hz[g] *= pow2f(-fix_exp(qa[g], S::level_max(lv)));
   }
 
   float m_run[GG], l_lane[GG];
@@ -879,7 +896,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   lds_barrier();
 #pragma unroll
   for (int g = 0; g < GG; ++g)
-    hs[g] = S::kIntLut ? pow2f(-fix_exp(qa[g], fmaxf(fabsf(lv[0]), fabsf(lv[S::COLS - 1])))) : 1.0f;
+    hs[g] = S::kIntLut ? pow2f(-fix_exp(qa[g], S::level_max(lv))) : 1.0f;
 
   for (; c < n_stop; c += 2 * STR) {
     fetch(c + STR, wb, nb);

@@ -47,10 +47,12 @@ __device__ __forceinline__ void add_into(uint32_t* acc, int4 e) {
 __device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23); }
 
 // Exponent of the fixed-point scale of one head's score table.  With A = sum_i |q'_i| and cmax the largest
-// level magnitude, any sum of one entry per coordinate is at most A * cmax in magnitude; the scale 2^e with
-// e = 29 - floor(log2(A * cmax)) keeps that below 2^30, and each entry's rounding error is at most 2^-(e+1)
-// <= A * cmax * 2^-30.  For A * cmax = 0 or below the normal range e is clamped to 126 (the entries are
-// then 0 or rounded to 0); for infinite or NaN A the table is meaningless, as the query is.
+// level magnitude, any sum of one entry per table row is at most A * cmax in magnitude; the scale 2^e with
+// e = 29 - floor(log2(A * cmax)) keeps that below 2^30.  An entry is its fp32 value (relative error
+// ~2^-23 per product and sum) rounded to an integer (at most 2^-(e+1) <= A * cmax * 2^-30 more), so a
+// score's error stays orders of magnitude below 1e-4 |q| |k|.  For A * cmax = 0 or below the normal
+// range e is clamped to 126 (the entries are then 0 or rounded to 0); for infinite or NaN A the table is
+// meaningless, as the query is.
 __device__ __forceinline__ int fix_exp(float a, float cmax) {
   const uint32_t bits = __builtin_bit_cast(uint32_t, a * cmax);
   const int k = (int)((bits >> 23) & 0xffu) - 127;
