@@ -358,3 +358,83 @@ def pq_decode_attn(cent, q, codes, v, scale: float, seq_lens=None) -> np.ndarray
                                _p(v), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int64(T),
                                None if lens is None else _p(lens), ctypes.c_double(scale), _p(out))
     return out
+
+
+# --------------------------------------------------------------------------
+# Power-of-two key codec (shift-accumulate attention page, English abstract):
+# sign + index of a magnitude 2^-j (or, with the mantissa term, a sum of two
+# neighbouring powers of two) per element, times a per-key scale max |k_i|
+# --------------------------------------------------------------------------
+
+def pot_levels(b: int, mantissa: int):
+    """(magnitudes [2^(b-1)] descending, midpoints [2^(b-1) - 1])."""
+    n = 1 << (b - 1)
+    mags = np.zeros(8)
+    thr = np.zeros(7)
+    _load().ora_pot_levels(ctypes.c_int(b), ctypes.c_int(int(mantissa)), _p(mags), _p(thr))
+    return mags[:n].copy(), thr[:n - 1].copy()
+
+
+def pot_encode(keys, b: int, mantissa: int, tie_eps: float = 1e-6):
+    """Encode keys [..., d]: (codes [..., d*b/8] uint8, scales [...] = max |k_i|, tie [..., d] bool)."""
+    keys = _f64(keys)
+    d = keys.shape[-1]
+    lead = keys.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    bpk = d * b // 8
+    codes = np.zeros((n, bpk), dtype=np.uint8)
+    scales = np.zeros(n)
+    tie = np.zeros((n, d), dtype=np.uint8)
+    _load().ora_pot_encode(ctypes.c_int(d), ctypes.c_int(b), ctypes.c_int(int(mantissa)), _p(keys),
+                           ctypes.c_int64(n), _p(codes), _p(scales), _p(tie), ctypes.c_double(tie_eps))
+    return codes.reshape(lead + (bpk,)), scales.reshape(lead), tie.reshape(lead + (d,)).astype(bool)
+
+
+def pot_dequant(codes, scales, d: int, b: int, mantissa: int) -> np.ndarray:
+    """Rows [..., d] = scale * (-1)^sign * magnitude(index)."""
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    lead = codes.shape[:-1]
+    assert codes.shape[-1] == d * b // 8
+    scales = _f64(scales)
+    assert scales.shape == lead
+    n = int(np.prod(lead)) if lead else 1
+    out = np.zeros(lead + (d,))
+    _load().ora_pot_dequant(ctypes.c_int(d), ctypes.c_int(b), ctypes.c_int(int(mantissa)), _p(codes), _p(scales),
+                            ctypes.c_int64(n), _p(out))
+    return out
+
+
+def pot_scores(q, codes, scales, b: int, mantissa: int, seq_lens=None) -> np.ndarray:
+    """Raw scores [B, Hq, T]: scale_t * sum_i of q_i sign-flipped and shifted by the code's shift amounts."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    _, Hkv, T, bpk = codes.shape
+    assert bpk == d * b // 8
+    scales = _f64(scales)
+    assert scales.shape == (B, Hkv, T)
+    lens = _lens(seq_lens, B)
+    out = np.zeros((B, Hq, T))
+    _load().ora_pot_scores(ctypes.c_int(d), ctypes.c_int(b), ctypes.c_int(int(mantissa)), _p(q), _p(codes),
+                           _p(scales), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int64(T),
+                           None if lens is None else _p(lens), _p(out))
+    return out
+
+
+def pot_decode_attn(q, codes, scales, v, b: int, mantissa: int, scale: float, seq_lens=None) -> np.ndarray:
+    """Attention output [B, Hq, d] = softmax(scale * pot_scores) V, V [B, Hkv, T, d]."""
+    q = _f64(q)
+    B, Hq, d = q.shape
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    _, Hkv, T, bpk = codes.shape
+    assert bpk == d * b // 8
+    scales = _f64(scales)
+    v = _f64(v)
+    assert v.shape == (B, Hkv, T, d)
+    lens = _lens(seq_lens, B)
+    out = np.zeros((B, Hq, d))
+    _load().ora_pot_decode_attn(ctypes.c_int(d), ctypes.c_int(b), ctypes.c_int(int(mantissa)), _p(q), _p(codes),
+                                _p(scales), _p(v), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv),
+                                ctypes.c_int64(T), None if lens is None else _p(lens), ctypes.c_double(scale),
+                                _p(out))
+    return out

@@ -40,6 +40,14 @@
  *   - sign-pattern selection ranks a candidate by the attention-output error
  *     sum ||o_hat - o||^2 / sum ||o||^2 over all calibration rows (the pages
  *     rank by perplexity, which needs a model); ties go to the lowest index.
+ *   - power-of-two key codec ([SA] English abstract): a key element is stored
+ *     as a sign and the index j of a magnitude in a fixed descending set, times
+ *     a per-key scale alpha = max_i |k_i| (so every shift index is >= 0);
+ *     b bits = 1 sign bit (the top bit of the field) + b-1 index bits.  Plain
+ *     set: 2^-j.  With the one-term mantissa extension: 2^-(j/2) for even j and
+ *     2^-(j+1)/2 + 2^-(j+3)/2 = (3/4) 2^-(j-1)/2 for odd j.  The index is the
+ *     magnitude nearest to |k_i| / alpha in value (ties to the larger); there is
+ *     no zero magnitude; a zero key has alpha 0 and all codes 0.  No rotation.
  *
  * Everything is fp64.  Inputs arrive as double arrays (fp16/fp32 convert
  * exactly).  No blocking, no fusion, no reordering beyond the definitions.
@@ -587,6 +595,135 @@ void ora_pq_decode_attn(int d, int m, int K, const double* cent, const double* q
       const int kvh = h / G;
       softmax_av(d, s + ((size_t)bi * Hq + h) * Tcap, len, scale,
                  v + ((size_t)bi * Hkv + kvh) * Tcap * d, out + ((size_t)bi * Hq + h) * d);
+    }
+  }
+  free(s);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Power-of-two key codec.  [SA] English abstract: the key cache holds a     */
+/* signed power-of-two code per element, so that each product in q.k is a    */
+/* sign flip and a shift; a sub-power mantissa term adds one more shift for   */
+/* half the error.  Readings: see the header.                                 */
+/* ------------------------------------------------------------------------- */
+
+/* Shift amounts that make up magnitude j: returns their count (1 or 2). */
+static int pot_shifts(int mant, int j, int* r) {
+  if (!mant) { r[0] = j; return 1; }
+  if (j % 2 == 0) { r[0] = j / 2; return 1; }
+  r[0] = (j + 1) / 2;
+  r[1] = (j + 3) / 2;
+  return 2;
+}
+
+/* Magnitudes [2^(b-1)] (descending) and the midpoints between neighbours
+ * [2^(b-1) - 1]. */
+void ora_pot_levels(int b, int mant, double* mags, double* thresholds) {
+  const int n = 1 << (b - 1);
+  for (int j = 0; j < n; ++j) {
+    int r[2];
+    const int c = pot_shifts(mant, j, r);
+    mags[j] = 0.0;
+    for (int k = 0; k < c; ++k) mags[j] += ldexp(1.0, -r[k]);
+  }
+  for (int j = 0; j + 1 < n; ++j) thresholds[j] = 0.5 * (mags[j] + mags[j + 1]);
+}
+
+/* Encode n keys [n][d] into codes [n][d*b/8] (LSB-first b-bit fields: index
+ * in the low b-1 bits, sign in the top bit) and scales [n] = max_i |k_i|.
+ * tie [n][d] (may be NULL) = 1 where |k_i| lies within tie_eps * alpha of a
+ * midpoint times alpha. */
+void ora_pot_encode(int d, int b, int mant, const double* keys, int64_t n, uint8_t* codes, double* scales,
+                    uint8_t* tie, double tie_eps) {
+  const int nm = 1 << (b - 1);
+  const int bpk = d * b / 8;
+  double mags[8], thr[7];
+  ora_pot_levels(b, mant, mags, thr);
+  for (int64_t r = 0; r < n; ++r) {
+    const double* k = keys + (size_t)r * d;
+    double alpha = 0.0;
+    for (int i = 0; i < d; ++i)
+      if (fabs(k[i]) > alpha) alpha = fabs(k[i]);
+    scales[r] = alpha;
+    uint8_t* row = codes + (size_t)r * bpk;
+    memset(row, 0, (size_t)bpk);
+    for (int i = 0; i < d; ++i) {
+      int j = 0, sgn = 0;
+      uint8_t f = 0;
+      if (alpha > 0.0) {
+        const double x = fabs(k[i]);
+        for (int m = 0; m + 1 < nm; ++m) {
+          if (x < thr[m] * alpha) j += 1;  /* below the midpoint: a smaller magnitude is nearer */
+          if (fabs(x - thr[m] * alpha) < tie_eps * alpha) f = 1;
+        }
+        sgn = k[i] < 0.0 ? 1 : 0;
+      }
+      put_code(row, i, b, j | (sgn << (b - 1)));
+      if (tie) tie[(size_t)r * d + i] = f;
+    }
+  }
+}
+
+/* Dequantized rows [n][d]: alpha * (-1)^sign * magnitude(j). */
+void ora_pot_dequant(int d, int b, int mant, const uint8_t* codes, const double* scales, int64_t n, double* out) {
+  const int bpk = d * b / 8;
+  double mags[8], thr[7];
+  ora_pot_levels(b, mant, mags, thr);
+  for (int64_t r = 0; r < n; ++r)
+    for (int i = 0; i < d; ++i) {
+      const int c = get_code(codes + (size_t)r * bpk, i, b);
+      const int j = c & ((1 << (b - 1)) - 1), sgn = c >> (b - 1);
+      out[(size_t)r * d + i] = scales[r] * (sgn ? -mags[j] : mags[j]);
+    }
+}
+
+/* Score of one key: alpha * sum_i of the query element, sign-flipped and
+ * shifted right by each shift amount of the element's magnitude. */
+static double pot_score(int d, int b, int mant, const double* q, const uint8_t* row, double alpha) {
+  double acc = 0.0;
+  for (int i = 0; i < d; ++i) {
+    const int c = get_code(row, i, b);
+    const int j = c & ((1 << (b - 1)) - 1);
+    const double x = (c >> (b - 1)) ? -q[i] : q[i];
+    int r[2];
+    const int cnt = pot_shifts(mant, j, r);
+    for (int k = 0; k < cnt; ++k) acc += ldexp(x, -r[k]);
+  }
+  return alpha * acc;
+}
+
+/* Raw scores [B][Hq][Tcap] from codes [B][Hkv][Tcap][d*b/8] and scales
+ * [B][Hkv][Tcap]; positions t >= seq_len[b] are -inf. */
+void ora_pot_scores(int d, int b, int mant, const double* q, const uint8_t* codes, const double* scales, int B,
+                    int Hq, int Hkv, int64_t Tcap, const int32_t* seq_lens, double* scores) {
+  const int bpk = d * b / 8;
+  const int G = Hq / Hkv;
+  for (int bi = 0; bi < B; ++bi) {
+    const int64_t len = seq_len_of(seq_lens, bi, Tcap);
+    for (int h = 0; h < Hq; ++h) {
+      const double* qh = q + ((size_t)bi * Hq + h) * d;
+      double* srow = scores + ((size_t)bi * Hq + h) * Tcap;
+      for (int64_t t = 0; t < Tcap; ++t) {
+        if (t >= len) { srow[t] = -INFINITY; continue; }
+        const size_t key = ((size_t)bi * Hkv + h / G) * Tcap + t;
+        srow[t] = pot_score(d, b, mant, qh, codes + key * bpk, scales[key]);
+      }
+    }
+  }
+}
+
+/* Decode attention with power-of-two key codes: softmax(scale * scores) . V. */
+void ora_pot_decode_attn(int d, int b, int mant, const double* q, const uint8_t* codes, const double* scales,
+                         const double* v, int B, int Hq, int Hkv, int64_t Tcap, const int32_t* seq_lens,
+                         double scale, double* out) {
+  const int G = Hq / Hkv;
+  double* s = (double*)malloc(sizeof(double) * (size_t)B * Hq * (Tcap > 0 ? Tcap : 1));
+  ora_pot_scores(d, b, mant, q, codes, scales, B, Hq, Hkv, Tcap, seq_lens, s);
+  for (int bi = 0; bi < B; ++bi) {
+    const int64_t len = seq_len_of(seq_lens, bi, Tcap);
+    for (int h = 0; h < Hq; ++h) {
+      const double* vh = v + ((size_t)bi * Hkv + h / G) * Tcap * d;
+      softmax_av(d, s + ((size_t)bi * Hq + h) * Tcap, len, scale, vh, out + ((size_t)bi * Hq + h) * d);
     }
   }
   free(s);

@@ -664,3 +664,129 @@ def test_decode_attn_qv_special_cases(oracle_mod):
     np.testing.assert_array_equal(out[1], 0.0)
     out0 = oracle_mod.decode_attn_qv(lv, s, q, codes, norms, vcodes, vnorms, 0.125, seq_lens=[0, 5])
     np.testing.assert_array_equal(out0[0], 0.0)
+
+
+# ---------------------------------------------------------------------------------------------------------
+# Power-of-two key codec (shift-accumulate attention page, English abstract)
+# ---------------------------------------------------------------------------------------------------------
+
+POT_CASES = [(b, m) for b in (2, 3, 4) for m in (0, 1)]
+
+
+@pytest.mark.parametrize("b,mant", POT_CASES)
+def test_pot_magnitudes_are_powers_of_two_or_one_extra_term(oracle_mod, b, mant):
+    """Every magnitude is 2^-r (plain code) or, with the mantissa term, 2^-r or 2^-r + 2^-(r+1); the set
+    descends from 1, so alpha = max|k| leaves every shift non-negative; midpoints sit between neighbours."""
+    mags, thr = oracle_mod.pot_levels(b, mant)
+    assert len(mags) == 1 << (b - 1) and mags[0] == 1.0
+    assert np.all(np.diff(mags) < 0)
+    for x in mags:
+        r = -math.floor(math.log2(x))
+        rest = x - 2.0 ** -r
+        assert rest == 0.0 or (mant == 1 and rest == 2.0 ** -(r + 1)), x
+    np.testing.assert_array_equal(thr, (mags[:-1] + mags[1:]) / 2)
+
+
+def test_pot_hand_packed_example(oracle_mod):
+    """A key worked by hand (plain 4-bit code: sign in bit 3, index j in bits 0..2, magnitude 2^-j, scale 4):
+    x = |k|/4 = 1, .5, .25, .15, .1, 0, .8, .7, .75 (a midpoint: the larger magnitude), .375 (a midpoint),
+    .0125, .0025, .0625, .03125, .015625, 1 -> j = 0,1,2,3,3,7,0,1,0,1,6,7,4,5,6,0 with the signs of k;
+    codes 0,9,2,3,11,7,0,9,0,1,14,7,4,13,6,8 packed two per byte, low nibble first."""
+    k = np.array([4.0, -2.0, 1.0, 0.6, -0.4, 0.0, 3.2, -2.8, 3.0, 1.5, -0.05, 0.01, 0.25, -0.125, 0.0625, -4.0])
+    codes, scales, tie = oracle_mod.pot_encode(k[None, :], 4, 0)
+    assert scales[0] == 4.0
+    assert list(codes[0]) == [0x90, 0x32, 0x7B, 0x90, 0x10, 0x7E, 0xD4, 0x86]
+    assert tie[0, 8] and tie[0, 9] and tie.sum() == 2
+    khat = 4.0 * np.array([1, -.5, .25, .125, -.125, 2 ** -7, 1, -.5, 1, .5, -2 ** -6, 2 ** -7, 2 ** -4, -2 ** -5,
+                           2 ** -6, -1])
+    np.testing.assert_array_equal(oracle_mod.pot_dequant(codes, scales, 16, 4, 0)[0], khat)
+    s = oracle_mod.pot_scores(np.ones((1, 1, 16)), codes[None, None], scales[None, None], 4, 0)
+    assert s[0, 0, 0] == 7.1875 == khat.sum()
+    # the same key with the mantissa term: magnitudes 1, 3/4, 1/2, 3/8, 1/4, 3/16, 1/8, 3/32
+    c1, _, _ = oracle_mod.pot_encode(k[None, :], 4, 1)
+    j1 = oracle_mod.unpack_codes(c1, 16, 4)[0]
+    # x = .8, .7 and .75 now take 3/4 (j = 1); .15 takes 1/8 (j = 6: |.15 - .125| < |.15 - .1875|); .1 and
+    # everything smaller take 3/32 (j = 7), the smallest magnitude
+    assert list(j1 & 7) == [0, 2, 4, 6, 7, 7, 1, 1, 1, 3, 7, 7, 7, 7, 7, 0]
+    assert list(j1 >> 3) == [0, 1, 0, 0, 1, 0, 0, 1, 0, 0, 1, 0, 0, 1, 0, 1]
+
+
+@pytest.mark.parametrize("b,mant", POT_CASES)
+def test_pot_encode_is_the_nearest_magnitude(oracle_mod, b, mant):
+    """Brute force: the decoded index is argmin_j | |k_i|/alpha - mag_j | (ties to the larger magnitude),
+    the sign bit is k_i < 0, alpha = max |k_i|."""
+    rng = np.random.default_rng(100 + 10 * b + mant)
+    k = rng.standard_normal((300, 32)) * np.exp(rng.standard_normal((300, 1)))
+    k = k.astype(np.float16).astype(np.float64)
+    codes, scales, tie = oracle_mod.pot_encode(k, b, mant)
+    np.testing.assert_array_equal(scales, np.abs(k).max(axis=1))
+    mags, _ = oracle_mod.pot_levels(b, mant)
+    idx = oracle_mod.unpack_codes(codes, 32, b)
+    j, sgn = idx & ((1 << (b - 1)) - 1), idx >> (b - 1)
+    x = np.abs(k) / scales[:, None]
+    ref = np.argmin(np.abs(x[..., None] - mags), axis=-1)
+    np.testing.assert_array_equal(j[~tie], ref[~tie])
+    np.testing.assert_array_equal(sgn, (k < 0).astype(sgn.dtype))
+
+
+@pytest.mark.parametrize("b,mant,bound", [(4, 0, 1 / 3), (4, 1, 1 / 5), (3, 0, 1 / 3), (3, 1, 1 / 5)])
+def test_pot_relative_error_closed_form(oracle_mod, b, mant, bound):
+    """Nearest power of two in value is off by at most 1/3 of the element (at 3/4 of an octave), and the
+    mantissa term brings that to 1/5 (at 5/8); both bounds are reached, at every scale in range."""
+    mags, _ = oracle_mod.pot_levels(b, mant)
+    x = np.geomspace(mags[-1], 1.0, 40001)
+    key = np.concatenate([[1.0], x])  # alpha = 1
+    rows = key[: (len(key) // 16) * 16].reshape(-1, 16)
+    rows[:, 0] = 1.0
+    codes, scales, _ = oracle_mod.pot_encode(rows, b, mant)
+    khat = oracle_mod.pot_dequant(codes, scales, 16, b, mant)
+    rel = np.abs(khat - rows) / rows
+    assert rel.max() <= bound + 1e-12
+    assert rel.max() >= bound - 1e-3
+
+
+def test_pot_scale_invariance_and_sign_mirror(oracle_mod):
+    rng = np.random.default_rng(7)
+    k = rng.standard_normal((50, 64))
+    k[3, :5] = 0.0
+    c0, s0, _ = oracle_mod.pot_encode(k, 4, 1)
+    for e in (-3, 1, 5):
+        c, s, _ = oracle_mod.pot_encode(k * 2.0 ** e, 4, 1)
+        np.testing.assert_array_equal(c, c0)
+        np.testing.assert_array_equal(s, s0 * 2.0 ** e)
+    cn, sn, _ = oracle_mod.pot_encode(-k, 4, 1)
+    np.testing.assert_array_equal(sn, s0)
+    i0, i1 = oracle_mod.unpack_codes(c0, 64, 4), oracle_mod.unpack_codes(cn, 64, 4)
+    np.testing.assert_array_equal(i1 & 7, i0 & 7)
+    np.testing.assert_array_equal(i1 >> 3, np.where(k != 0, 1 - (i0 >> 3), 0))
+
+
+def test_pot_zero_key(oracle_mod):
+    k = np.zeros((1, 1, 1, 16))
+    codes, scales, _ = oracle_mod.pot_encode(k, 4, 0)
+    assert scales.item() == 0.0 and not codes.any()
+    s = oracle_mod.pot_scores(np.ones((1, 1, 16)), codes, scales, 4, 0)
+    assert s.item() == 0.0
+
+
+@pytest.mark.parametrize("d,b,mant,G", [(16, 2, 0, 1), (64, 4, 0, 8), (64, 4, 1, 4), (128, 3, 1, 2)])
+def test_pot_scores_and_attention_equal_dequantized(oracle_mod, d, b, mant, G):
+    """Shift-and-add scores equal q . k_hat (a matrix product on the dequantized keys, GQA by repetition),
+    and the attention equals torch SDPA on the dequantized keys."""
+    rng = np.random.default_rng(d + b + mant + G)
+    B, Hkv, T = 2, 2, 37
+    Hq = Hkv * G
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, T, d)) * np.exp(0.5 * rng.standard_normal((B, Hkv, T, 1)))
+    v = rng.standard_normal((B, Hkv, T, d))
+    codes, scales, _ = oracle_mod.pot_encode(k, b, mant)
+    khat = oracle_mod.pot_dequant(codes, scales, d, b, mant)
+    s = oracle_mod.pot_scores(q, codes, scales, b, mant)
+    ref = np.matmul(q[:, :, None, :], np.repeat(khat, G, axis=1).transpose(0, 1, 3, 2))[:, :, 0, :]
+    np.testing.assert_allclose(s, ref, rtol=1e-12, atol=1e-12)
+    scale = 1.0 / math.sqrt(d)
+    out = oracle_mod.pot_decode_attn(q, codes, scales, v, b, mant, scale)
+    np.testing.assert_allclose(out, _torch_sdpa(q, khat, v, scale, G), rtol=1e-10, atol=1e-12)
+    lens = [T, 5]
+    s2 = oracle_mod.pot_scores(q, codes, scales, b, mant, seq_lens=lens)
+    assert np.all(np.isneginf(s2[1, :, 5:])) and np.array_equal(s2[1, :, :5], s[1, :, :5])
