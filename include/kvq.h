@@ -68,23 +68,26 @@ typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_F16 = 1 } kvq_dtype;
 
 typedef enum kvq_kind {
   KVQ_HADAMARD_LM = 0, /* Walsh-Hadamard rotation + Lloyd-Max scalar codebook */
-  KVQ_PQ = 1           /* product quantization, asymmetric distance computation */
+  KVQ_PQ = 1,          /* product quantization, asymmetric distance computation */
+  KVQ_POT = 2          /* signed power-of-two element codes with a per-key scale */
 } kvq_kind;
 
 #define KVQ_MAX_LEVELS 16
 
-/* A codebook.  Plain data: copy it freely.  For KVQ_HADAMARD_LM it is fully
- * described by (d, b) and the arrays; for KVQ_PQ it refers to caller-owned
- * device centroids. */
+/* A codebook.  Plain data: copy it freely.  For KVQ_HADAMARD_LM and KVQ_POT it
+ * is fully described by its sizes and the arrays; for KVQ_PQ it refers to
+ * caller-owned device centroids. */
 typedef struct kvq_codebook {
   int32_t kind;                            /* kvq_kind */
   int32_t d;                               /* head dimension */
-  int32_t b;                               /* HLM: bits per coordinate, 1..4 */
-  int32_t m;                               /* PQ: number of subspaces (d % m == 0) */
+  int32_t b;                               /* HLM: bits per coordinate, 1..4; POT: bits per element, 2..4 */
+  int32_t m;                               /* PQ: number of subspaces (d % m == 0); POT: 1 with the mantissa term */
   int32_t K;                               /* PQ: centroids per subspace, 2..256 */
   int32_t n_heads;                         /* PQ: kv heads covered by pq_centroids */
-  float levels[KVQ_MAX_LEVELS];            /* HLM: ascending levels c_0..c_{2^b-1} */
-  float thresholds[KVQ_MAX_LEVELS - 1];    /* HLM: t_j = (c_j + c_{j+1}) / 2 */
+  float levels[KVQ_MAX_LEVELS];            /* HLM: ascending levels c_0..c_{2^b-1};
+                                              POT: signed level of every code value */
+  float thresholds[KVQ_MAX_LEVELS - 1];    /* HLM: t_j = (c_j + c_{j+1}) / 2;
+                                              POT: midpoints of the descending magnitudes */
   const float* pq_centroids;               /* PQ: device [n_heads][m][K][d/m] fp32 */
 } kvq_codebook;
 
@@ -116,15 +119,31 @@ kvq_status kvq_build_codebook(int d, int b, kvq_codebook* out);
 kvq_status kvq_build_codebook_pq(const float* train, int H, int64_t n, int d, int m, int K, int iters,
                                  const int64_t* start_rows, float* centroids);
 
+/* Signed power-of-two element codes (shift-accumulate attention page, English
+ * abstract: keys as signed power-of-two fixed-point codes, so that every
+ * product in q.k is a sign flip and a shift, with an optional sub-power
+ * mantissa term).  Host only, deterministic.  A key k is stored as
+ * alpha = max_i |k_i| (in the norms buffer) and one b-bit field per element:
+ * bit b-1 = sign (k_i < 0), bits 0..b-2 = the index j of the magnitude nearest
+ * to |k_i| / alpha (ties to the larger) in the descending set
+ *   mantissa == 0:  2^-j,
+ *   mantissa == 1:  2^-(j/2) for even j, (3/4) 2^-((j-1)/2) for odd j.
+ * The element's value is alpha * (-1)^sign * magnitude(j); levels[c] holds
+ * (-1)^sign * magnitude(j) for every code value c, thresholds the midpoints.
+ * No rotation and no sign pattern (signs may be NULL in every call).
+ *   d: power of two, 16 <= d <= 256.   b: 2..4.   mantissa: 0 or 1.
+ * Errors: KVQ_ERR_INVALID_ARG for d, b, mantissa out of range or out == NULL. */
+kvq_status kvq_build_codebook_pot(int d, int b, int mantissa, kvq_codebook* out);
+
 /* Fill a KVQ_PQ codebook that refers to device centroids
  * [n_heads][m][K][d/m] fp32 (caller-owned; must outlive every call using
  * the codebook).  Host only. */
 kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centroids_device, kvq_codebook* out);
 
 /* Write path: encode keys into the code cache (AXELRAM, Abstract: transform on
- * write).
- *   cb:        codebook (HLM or PQ).
- *   signs:     host [d] int8, each +1 or -1 (HLM); ignored for PQ (may be NULL).
+ * write; for KVQ_POT the shift-accumulate page's power-of-two code).
+ *   cb:        codebook (HLM, POT or PQ).
+ *   signs:     host [d] int8, each +1 or -1 (HLM); ignored for POT and PQ (may be NULL).
  *   keys:      device [B][Hkv][T_new][d], dtype kdtype (may be NULL when T_new == 0).
  *   codes:     device [B][Hkv][T_cap][d*b/8] (HLM) or [B][Hkv][T_cap][m] (PQ)
  *              uint8; rows pos_b .. pos_b+T_new-1 of every (b, h) are written.
@@ -144,7 +163,9 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
                            int64_t t0, const int32_t* write_pos, void* stream);
 
 /* Read path, scores only (AXELRAM, Abstract: table lookup on read; LOOKAT for
- * PQ).  scores[b][h][t] = raw estimate of q.k_t (no softmax scale) for
+ * PQ; for POT the table holds the query elements sign-flipped and shifted by
+ * each magnitude, so a score is a sum of shifted query elements times alpha).
+ * scores[b][h][t] = raw estimate of q.k_t (no softmax scale) for
  * t < len_b; scores at t >= len_b are set to -inf.
  *   q:        device [B][Hq][d], dtype qdtype.
  *   codes, norms: as written by kvq_encode_keys (norms ignored for PQ).
@@ -200,7 +221,7 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
  *   codes, norms: the cache, read and written (rows len_b - 1).
  *   Every other argument as kvq_decode_attn, including the workspace (same
  *   size, from kvq_decode_attn_workspace).
- * Errors: as kvq_decode_attn; KVQ_ERR_UNSUPPORTED for a PQ codebook. */
+ * Errors: as kvq_decode_attn; KVQ_ERR_UNSUPPORTED for a PQ or POT codebook. */
 kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, const void* new_keys,
                                   kvq_dtype kdtype, const void* q, kvq_dtype qdtype, uint8_t* codes, float* norms,
                                   const void* v, kvq_dtype vdtype, int B, int Hq, int Hkv, int64_t T_cap,
@@ -220,7 +241,7 @@ kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, c
  *   (kvq_decode_attn_workspace) and the errors are those of kvq_decode_attn.
  *   The products run in fp16 with fp32 accumulation: |v_t| times a level
  *   must stay within the fp16 range.
- * Hadamard/Lloyd-Max codebooks only (KVQ_ERR_UNSUPPORTED for PQ). */
+ * Hadamard/Lloyd-Max codebooks only (KVQ_ERR_UNSUPPORTED for PQ and POT). */
 kvq_status kvq_decode_attn_qv(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
                               const uint8_t* codes, const float* norms, const uint8_t* vcodes, const float* vnorms,
                               int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale, void* out,

@@ -48,6 +48,13 @@ kvq_status check_codebook(const kvq_codebook* cb) {
     if (cb->b < 1 || cb->b > 4) return fail(KVQ_ERR_INVALID_ARG, "b=%d: must be 1..4", cb->b);
     return KVQ_OK;
   }
+  if (cb->kind == KVQ_POT) {
+    if (!pow2(cb->d) || cb->d < 16 || cb->d > 256)
+      return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", cb->d);
+    if (cb->b < 2 || cb->b > 4) return fail(KVQ_ERR_INVALID_ARG, "power-of-two b=%d: must be 2..4", cb->b);
+    if (cb->m != 0 && cb->m != 1) return fail(KVQ_ERR_INVALID_ARG, "power-of-two mantissa flag %d: must be 0 or 1", cb->m);
+    return KVQ_OK;
+  }
   if (cb->kind == KVQ_PQ) {
     if (cb->d <= 0 || cb->m <= 0 || cb->d % cb->m != 0)
       return fail(KVQ_ERR_INVALID_ARG, "PQ d=%d, m=%d: m must divide d", cb->d, cb->m);
@@ -140,6 +147,10 @@ kvq_status check_read(const kvq_codebook* cb, const int8_t* signs, const void* q
     st = pack_signs(signs, cb->d, p->signs);
     if (st != KVQ_OK) return st;
     for (int j = 0; j < 16; ++j) p->levels[j] = j < (1 << cb->b) ? cb->levels[j] : 0.0f;
+  } else if (cb->kind == KVQ_POT) {
+    if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms (per-key scales) is NULL");
+    if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
+    for (int j = 0; j < 16; ++j) p->levels[j] = j < (1 << cb->b) ? cb->levels[j] : 0.0f;
   } else {
     if (cb->n_heads != Hkv) return fail(KVQ_ERR_INVALID_ARG, "PQ codebook has %d heads, Hkv=%d", cb->n_heads, Hkv);
     p->pq_cent = cb->pq_centroids;
@@ -194,6 +205,25 @@ kvq_status kvq_build_codebook(int d, int b, kvq_codebook* out) {
   out->kind = KVQ_HADAMARD_LM;
   out->d = d;
   out->b = b;
+  return ok();
+}
+
+kvq_status kvq_build_codebook_pot(int d, int b, int mantissa, kvq_codebook* out) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+  if (!pow2(d) || d < 16 || d > 256) return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", d);
+  if (b < 2 || b > 4) return fail(KVQ_ERR_INVALID_ARG, "b=%d: must be 2..4", b);
+  if (mantissa != 0 && mantissa != 1) return fail(KVQ_ERR_INVALID_ARG, "mantissa=%d: must be 0 or 1", mantissa);
+  std::memset(out, 0, sizeof *out);
+  const int nm = 1 << (b - 1);
+  double mag[8];
+  for (int j = 0; j < nm; ++j)  // 2^-j, or with the mantissa term 2^-(j/2) and (3/4) 2^-((j-1)/2) alternately
+    mag[j] = mantissa ? std::ldexp(j % 2 ? 0.75 : 1.0, -(j / 2)) : std::ldexp(1.0, -j);
+  for (int c = 0; c < 2 * nm; ++c) out->levels[c] = (float)(c >= nm ? -mag[c - nm] : mag[c]);
+  for (int j = 0; j + 1 < nm; ++j) out->thresholds[j] = (float)(0.5 * (mag[j] + mag[j + 1]));
+  out->kind = KVQ_POT;
+  out->d = d;
+  out->b = b;
+  out->m = mantissa;
   return ok();
 }
 
@@ -274,6 +304,17 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
     if (T_new == 0) return ok();
     return from_hip(kvq::launch_hlm_encode(cb->d, cb->b, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
   }
+  if (cb->kind == KVQ_POT) {
+    if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms (per-key scales) is NULL");
+    if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
+    for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << (cb->b - 1)) ? cb->thresholds[j] : 0.0f;
+    if (T_new > 0 && (int64_t)B * Hkv * T_new >= ((int64_t)1 << 31))
+      return fail(KVQ_ERR_UNSUPPORTED, "B*Hkv*T_new must stay below 2^31");
+    if (T_new > 0) kvq::fast_div_magic((uint32_t)T_new, &p.tnew_magic, &p.tnew_shift);
+    kvq::fast_div_magic((uint32_t)Hkv, &p.hkv_magic, &p.hkv_shift);
+    if (T_new == 0) return ok();
+    return from_hip(kvq::launch_pot_encode(cb->d, cb->b, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
+  }
   if (cb->n_heads != Hkv) return fail(KVQ_ERR_INVALID_ARG, "PQ codebook has %d heads, Hkv=%d", cb->n_heads, Hkv);
   p.pq_cent = cb->pq_centroids;
   p.pq_K = cb->K;
@@ -295,6 +336,7 @@ kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q,
   const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cb->kind == KVQ_HADAMARD_LM) return from_hip(kvq::launch_hlm_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");
+  if (cb->kind == KVQ_POT) return from_hip(kvq::launch_pot_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");
   return from_hip(kvq::launch_pq_score(cb->d, cb->m, rs.gg, p, grid, s), "kvq_score");
 }
 
@@ -357,9 +399,9 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
   }
   const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = cb->kind == KVQ_HADAMARD_LM
-                     ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
-                     : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
+  hipError_t e = cb->kind == KVQ_HADAMARD_LM ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
+                 : cb->kind == KVQ_POT      ? kvq::launch_pot_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
+                                            : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
   return from_hip(e, name);
 }
 

@@ -60,13 +60,14 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int i) {
   return x & ((1u << B) - 1u);
 }
 
-// Scorer for the Hadamard + Lloyd-Max codec.  A table row covers GRP consecutive coordinates whose codes
-// fill one 4-bit field of the packed row (GRP = 4 / b for b = 1, 2, 4; one coordinate for b = 3): its
-// column is that field, and entry (r, n) = sum_k q'_{r GRP + k} * c_{code_k(n)} with code_k(n) the k-th b-bit
-// part of n.  So every table lookup adds 4 bits' worth of codes, and a key takes d b / 4 lookups (d for
-// b = 3) however many coordinates a row spans.
+// Table of a scalar codec (one b-bit code per coordinate, one level per code value, a per-key factor
+// stored beside the codes).  A table row covers GRP consecutive coordinates whose codes fill one 4-bit
+// field of the packed row (GRP = 4 / b for b = 1, 2, 4; one coordinate for b = 3): its column is that
+// field, and entry (r, n) = sum_k q'_{r GRP + k} * lv[code_k(n)] with code_k(n) the k-th b-bit part of n and
+// lv the level of each code value.  So every table lookup adds 4 bits' worth of codes, and a key takes
+// d b / 4 lookups (d for b = 3) however many coordinates a row spans.
 template <int D_, int BITS>
-struct HlmScorer {
+struct ScalarTable {
   static constexpr int D = D_;
   static constexpr int LEVELS = 1 << BITS;
   static constexpr int GRP = BITS == 3 ? 1 : 4 / BITS;  // coordinates per table row
@@ -75,13 +76,17 @@ struct HlmScorer {
   static constexpr int CODE_BITS = BITS;
   static constexpr int BPK = D * BITS / 8;
   static constexpr int NW = (BPK + 3) / 4;
-  static constexpr bool kRotate = true;
   static constexpr bool kNorm = true;
   static constexpr bool kNibbles = BITS * GRP == 4;  // rows indexed by the 4-bit fields of the packed codes
   static constexpr bool kIntLut = true;              // fixed-point table entries, summed exactly in 32-bit integers
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) { return code_at<BITS, NW>(w, i); }
-  __device__ static __forceinline__ float level_max(const float* lv) { return fmaxf(fabsf(lv[0]), fabsf(lv[LEVELS - 1])); }
-  // Table of head g, with q' = H D q / sqrt(d) held in qs: every entry is the integer nearest to its value
+  __device__ static __forceinline__ float level_max(const float* lv) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < LEVELS; ++j) m = fmaxf(m, fabsf(lv[j]));
+    return m;
+  }
+  // Table of head g, with the (transformed) query q' held in qs: every entry is the integer nearest to its value
   // times 2^e_g (fix_exp), so the table of head g sums to at most 2^30 in magnitude along any choice of one
   // entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
   // column); each work item fills JPT consecutive columns of one (head group, row).
@@ -123,6 +128,22 @@ struct HlmScorer {
       }
     }
   }
+};
+
+// Hadamard + Lloyd-Max codec: the query is rotated, q' = H D q / sqrt(d), and the levels are the Lloyd-Max
+// levels of N(0, 1/d); the per-key factor is the key norm.
+template <int D_, int BITS>
+struct HlmScorer : ScalarTable<D_, BITS> {
+  static constexpr bool kRotate = true;
+};
+
+// Power-of-two codec (shift-accumulate attention page, English abstract): no rotation, q' = q; the level of
+// code value c is (-1)^sign * 2^-j (or (3/4) 2^-j', the mantissa term), so a table entry is a query element
+// with its sign flipped and shifted (for fp16 queries the scaled entries are the exact shifted integers
+// whenever the element is at least 2^-10 of the query's sum of magnitudes); the per-key factor is max |k_i|.
+template <int D_, int BITS>
+struct PotScorer : ScalarTable<D_, BITS> {
+  static constexpr bool kRotate = false;
 };
 
 // Scorer for product quantization: rows = subspaces, cols = centroids (<= 256).
@@ -203,10 +224,11 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
   return r;
 }
 
-// Loads the GG queries into qs[g][i] (fp32) and copies the codebook levels into LDS.  For the Hadamard
-// codec every query is also rotated, q' = H D q / sqrt(d): 8 consecutive coordinates per lane and d/8
-// lanes per query, sign flip, then a radix-2 fast Walsh-Hadamard transform (Sylvester order) in registers
-// (distances 1, 2, 4) and across the query's lanes (distances 8 .. d/2).
+// Loads the GG queries into qs[g][i] (fp32) and copies the codebook levels into LDS.  For the scalar codecs
+// (fixed-point tables) a query takes 8 consecutive coordinates per lane and d/8 lanes, and qa[g] receives
+// sum_i |q'_{g,i}|, the bound that sets the head's table scale.  For the Hadamard codec every query is also
+// rotated, q' = H D q / sqrt(d): sign flip, then a radix-2 fast Walsh-Hadamard transform (Sylvester order)
+// in registers (distances 1, 2, 4) and across the query's lanes (distances 8 .. d/2).
 // `between` runs after this thread's query loads are issued and before they are used: the caller issues
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
@@ -214,7 +236,7 @@ template <class S, int GG, class F>
 __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
   if (tid < 16) lv[tid] = p.levels[tid];
-  if constexpr (S::kRotate) {
+  if constexpr (S::kIntLut) {
     constexpr int LPQ = D / 8;  // lanes per query (a power of two <= 32, so groups never straddle waves)
     static_assert(GG * LPQ <= kThreads, "one lane per 8 coordinates of every query");
     const int g = tid / LPQ, k = tid % LPQ;
@@ -247,28 +269,30 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
 #pragma unroll
         for (int t = 0; t < 8; ++t) x[t] = __builtin_bit_cast(float, r[t]);
       }
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if ((sb >> t) & 1u) x[t] = -x[t];
-#pragma unroll
-      for (int h = 1; h < 8; h <<= 1)
+      if constexpr (S::kRotate) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
-          if ((t & h) == 0) {
-            const float a = x[t], b = x[t + h];
-            x[t] = a + b;
-            x[t + h] = a - b;
+          if ((sb >> t) & 1u) x[t] = -x[t];
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if ((t & h) == 0) {
+              const float a = x[t], b = x[t + h];
+              x[t] = a + b;
+              x[t + h] = a - b;
+            }
+#pragma unroll
+        for (int dl = 1; dl < LPQ; dl <<= 1) {
+          const bool upper = (k & dl) != 0;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float o = __shfl_xor(x[t], dl, 64);
+            x[t] = upper ? (o - x[t]) : (x[t] + o);
           }
-#pragma unroll
-      for (int dl = 1; dl < LPQ; dl <<= 1) {
-        const bool upper = (k & dl) != 0;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float o = __shfl_xor(x[t], dl, 64);
-          x[t] = upper ? (o - x[t]) : (x[t] + o);
         }
       }
-      const float rs = 1.0f / __builtin_sqrtf((float)D);
+      const float rs = S::kRotate ? 1.0f / __builtin_sqrtf((float)D) : 1.0f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) qs[g * D + 8 * k + t] = x[t] * rs;
       if (qa != nullptr) {  // sum_i |q'_i| of the query: the bound that scales its fixed-point table
@@ -963,6 +987,27 @@ hipError_t run_hlm_score(int bits, int gg, const AttnParams& p, dim3 grid, hipSt
     case 2: return run_score<HlmScorer<D, 2>>(gg, p, grid, s);
     case 3: return run_score<HlmScorer<D, 3>>(gg, p, grid, s);
     case 4: return run_score<HlmScorer<D, 4>>(gg, p, grid, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+// Power-of-two codec dispatch for one head dimension (instantiated per D): 2..4 bits per element.
+template <int D>
+hipError_t run_pot_decode(int bits, int gg, bool v_f16, const AttnParams& p, dim3 grid, hipStream_t s) {
+  switch (bits) {
+    case 2: return run_decode<PotScorer<D, 2>>(gg, v_f16, p, grid, s);
+    case 3: return run_decode<PotScorer<D, 3>>(gg, v_f16, p, grid, s);
+    case 4: return run_decode<PotScorer<D, 4>>(gg, v_f16, p, grid, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+template <int D>
+hipError_t run_pot_score(int bits, int gg, const AttnParams& p, dim3 grid, hipStream_t s) {
+  switch (bits) {
+    case 2: return run_score<PotScorer<D, 2>>(gg, p, grid, s);
+    case 3: return run_score<PotScorer<D, 3>>(gg, p, grid, s);
+    case 4: return run_score<PotScorer<D, 4>>(gg, p, grid, s);
     default: return hipErrorNotSupported;
   }
 }

@@ -1,0 +1,107 @@
+// Write path of the power-of-two codec (shift-accumulate attention page, English abstract: the key cache
+// holds a signed power-of-two code per element, so that every product in q.k becomes a sign flip and a
+// shift, with an optional sub-power mantissa term).
+//
+// For every key k: alpha = max_i |k_i|; element i gets the index j of the magnitude nearest to |k_i| / alpha
+// in the codebook's descending set (|k_i| < t_m * alpha for exactly j of the midpoints t_m; a value on a
+// midpoint takes the larger magnitude) and the sign bit k_i < 0 above it; codes are packed LSB-first next
+// to alpha in the norms buffer.  No rotation.
+//
+// Layout: 8 elements per lane, D/8 lanes per key (a wave holds 64/(D/8) keys); alpha is reduced across the
+// key's lanes; each lane packs its 8*b bits and stores them at its own byte offset of the key's row.  For
+// fp16 keys every comparison is exact in fp32 (alpha has 11 significant bits and a midpoint at most 3).
+#include "encode_dev.h"
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+template <int LPK>
+__device__ __forceinline__ float key_lanes_max(float v) {
+  if constexpr (LPK >= 2) v = fmaxf(v, xor_lane<1>(v));
+  if constexpr (LPK >= 4) v = fmaxf(v, xor_lane<2>(v));
+  if constexpr (LPK >= 8) v = fmaxf(v, xor_lane<4>(v));
+  if constexpr (LPK >= 16) v = fmaxf(v, xor_lane<8>(v));
+  if constexpr (LPK >= 32) v = fmaxf(v, xor_lane<16>(v));
+  return v;
+}
+
+template <int D, int BITS, bool KF16>
+__global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
+  constexpr int LPK = D / 8;      // lanes per key
+  constexpr int KPB = 256 / LPK;  // keys per workgroup per pass
+  constexpr int BPK = D * BITS / 8;
+  constexpr int NM = 1 << (BITS - 1);  // magnitudes
+  const int lk = threadIdx.x & (LPK - 1);
+  const int64_t n_keys = p.key_end - p.key_begin;
+  const int64_t stride = (int64_t)gridDim.x * KPB;
+  auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t { return (__umulhi(n, magic) + n) >> shift; };
+  // every lane of a key takes the same trip count, so the cross-lane reduction sees all of them
+  for (int64_t k = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK; k < n_keys; k += stride) {
+    float x[8];
+    load_key_lane<D, KF16>(p.keys, p.key_begin + k, lk, x);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    const float alpha = key_lanes_max<LPK>(amax);
+    float lim[NM - 1];
+#pragma unroll
+    for (int m = 0; m < NM - 1; ++m) lim[m] = p.thresholds[m] * alpha;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float a = fabsf(x[j]);
+      uint32_t c = 0;
+#pragma unroll
+      for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
+      if (x[j] < 0.0f) c |= 1u << (BITS - 1);
+      packed |= c << (BITS * j);
+    }
+    const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
+    const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
+    const uint32_t t = gk - bh * (uint32_t)p.T_new;
+    int64_t pos = (int64_t)t;
+    if (p.write_pos) pos += p.write_pos[fdiv(bh, p.hkv_magic, p.hkv_shift)];
+    else pos += p.t0;
+    if (pos < 0 || pos >= p.T_cap) continue;
+    const int64_t row = (int64_t)bh * p.T_cap + pos;
+    store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
+    if (lk == 0) p.norms[row] = alpha;
+  }
+}
+
+template <int D, int BITS>
+static hipError_t pot_launch(bool kf16, const EncodeParams& p0, hipStream_t s) {
+  constexpr int KPB = 256 / (D / 8);
+  EncodeParams p = p0;
+  p.key_begin = 0;
+  p.key_end = (int64_t)p0.B * p0.Hkv * p0.T_new;
+  const int64_t blocks = (p.key_end + KPB - 1) / KPB;
+  const dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));
+  if (kf16) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t pot_d(int bits, bool kf16, const EncodeParams& p, hipStream_t s) {
+  switch (bits) {
+    case 2: return pot_launch<D, 2>(kf16, p, s);
+    case 3: return pot_launch<D, 3>(kf16, p, s);
+    case 4: return pot_launch<D, 4>(kf16, p, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+hipError_t launch_pot_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s) {
+  switch (D) {
+    case 16: return pot_d<16>(bits, k_f16, p, s);
+    case 32: return pot_d<32>(bits, k_f16, p, s);
+    case 64: return pot_d<64>(bits, k_f16, p, s);
+    case 128: return pot_d<128>(bits, k_f16, p, s);
+    case 256: return pot_d<256>(bits, k_f16, p, s);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace kvq

@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_DEVICE = range(5)
 KVQ_F32, KVQ_F16 = 0, 1
-KVQ_HADAMARD_LM, KVQ_PQ = 0, 1
+KVQ_HADAMARD_LM, KVQ_PQ, KVQ_POT = 0, 1, 2
 
 _STATUS = {1: "KVQ_ERR_INVALID_ARG", 2: "KVQ_ERR_UNSUPPORTED", 3: "KVQ_ERR_WORKSPACE", 4: "KVQ_ERR_DEVICE"}
 
@@ -49,7 +49,8 @@ class kvq_codebook(ctypes.Structure):
         return np.array(self.levels[: 1 << self.b], dtype=np.float32)
 
     def thresholds_array(self) -> np.ndarray:
-        return np.array(self.thresholds[: (1 << self.b) - 1], dtype=np.float32)
+        n = (1 << (self.b - 1)) - 1 if self.kind == KVQ_POT else (1 << self.b) - 1
+        return np.array(self.thresholds[:n], dtype=np.float32)
 
     @property
     def bytes_per_key(self) -> int:
@@ -67,6 +68,7 @@ _CB = ctypes.POINTER(kvq_codebook)
 _lib.kvq_version.restype = ctypes.c_int
 _lib.kvq_last_error.restype = ctypes.c_char_p
 _lib.kvq_build_codebook.argtypes = [_i32, _i32, _CB]
+_lib.kvq_build_codebook_pot.argtypes = [_i32, _i32, _i32, _CB]
 _lib.kvq_build_codebook_pq.argtypes = [_P, _i32, _i64, _i32, _i32, _i32, _i32, _P, _P]
 _lib.kvq_codebook_pq.argtypes = [_i32, _i32, _i32, _i32, _P, _CB]
 _lib.kvq_encode_keys.argtypes = [_CB, _P, _P, _i32, _i32, _i32, _i64, _P, _P, _i64, _i64, _P, _P]
@@ -83,11 +85,11 @@ _lib.kvq_select_signs_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
 _lib.kvq_select_signs_workspace.restype = _sz
 _lib.kvq_select_signs.argtypes = [_CB, _P, _i32, _P, _i32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i64, _f32, _P, _P,
                                   _P, _sz, _P]
-for _f in ("kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
+for _f in ("kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
            "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_qv", "kvq_select_signs"):
     getattr(_lib, _f).restype = ctypes.c_int
 
-EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pq", "kvq_codebook_pq",
+EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq",
            "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append",
            "kvq_decode_attn_qv", "kvq_select_signs_workspace", "kvq_select_signs")
 
@@ -147,6 +149,12 @@ def kvq_last_error() -> str:
 def kvq_build_codebook(d: int, b: int) -> kvq_codebook:
     cb = kvq_codebook()
     _check(_lib.kvq_build_codebook(d, b, ctypes.byref(cb)))
+    return cb
+
+
+def kvq_build_codebook_pot(d: int, b: int, mantissa: int = 0) -> kvq_codebook:
+    cb = kvq_codebook()
+    _check(_lib.kvq_build_codebook_pot(d, b, int(mantissa), ctypes.byref(cb)))
     return cb
 
 

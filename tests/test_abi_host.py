@@ -250,3 +250,39 @@ def test_decode_qv_validation(K):
     pq = K.kvq_codebook()
     K._check(lib.kvq_codebook_pq(64, 8, 256, 2, P(FAKE), ctypes.byref(pq)))
     assert call(cbx=pq) == K.KVQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("b", [2, 3, 4])
+@pytest.mark.parametrize("mant", [0, 1])
+def test_pot_codebook_matches_oracle(K, oracle_mod, b, mant):
+    """The power-of-two codebook: signed level per code value (sign in the top bit) and the midpoints of the
+    magnitudes, equal to the oracle's (all exact in fp32)."""
+    cb = K.kvq_build_codebook_pot(64, b, mant)
+    assert cb.kind == K.KVQ_POT and cb.b == b and cb.m == mant and cb.bytes_per_key == 64 * b // 8
+    mags, thr = oracle_mod.pot_levels(b, mant)
+    np.testing.assert_array_equal(cb.levels_array(), np.concatenate([mags, -mags]).astype(np.float32))
+    np.testing.assert_array_equal(cb.thresholds_array(), thr.astype(np.float32))
+
+
+def test_pot_validation(K):
+    for d, b, m in [(48, 4, 0), (512, 4, 0), (64, 1, 0), (64, 5, 0), (64, 4, 2)]:
+        with pytest.raises(K.KvqError) as e:
+            K.kvq_build_codebook_pot(d, b, m)
+        assert e.value.status == K.KVQ_ERR_INVALID_ARG
+    cb = K.kvq_build_codebook_pot(64, 4, 1)
+    # no sign pattern needed; scales (norms) are required
+    assert _call_encode(K, cb, None, norms=None) == K.KVQ_ERR_INVALID_ARG
+    assert "scales" in K.kvq_last_error()
+    bad = K.kvq_build_codebook_pot(64, 4, 1)
+    bad.m = 3
+    assert _call_encode(K, bad, None) == K.KVQ_ERR_INVALID_ARG
+    P = ctypes.c_void_p
+    lib = K._lib
+    assert lib.kvq_score(ctypes.byref(cb), None, P(FAKE), 1, P(FAKE), None, 1, 4, 2, 128, None, P(FAKE),
+                         None) == K.KVQ_ERR_INVALID_ARG
+    # the fused append and quantized values belong to the Hadamard codec
+    assert lib.kvq_decode_attn_append(ctypes.byref(cb), None, P(FAKE), 1, P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), 1,
+                                      1, 4, 2, 128, None, 0.125, P(FAKE), 1, P(FAKE), 1 << 20, 0,
+                                      None) == K.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_decode_attn_qv(ctypes.byref(cb), None, P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, 4, 2,
+                                  128, None, 0.125, P(FAKE), 1, P(FAKE), 1 << 20, 0, None) == K.KVQ_ERR_UNSUPPORTED
