@@ -264,7 +264,34 @@ def run_suite(K, torch, reps=5, calls=30):
 
         row(name, "decode-qv", timed(dec_qv, n_rot), B * Hkv * T * 2 * (bpk + 4) + B * Hq * d * 2, B * Hq * T,
             B * Hkv * T)
-        del caches, keys, scores, vcs
+        del vcs
+
+        # power-of-two key codes of the same width (shift-accumulate page), plain and with the mantissa term
+        for mant in ((0, 1) if b >= 2 else ()):
+            pcb = K.kvq_build_codebook_pot(d, b, mant)
+            pcs = []
+            for r in range(n_rot):
+                if r == 0:
+                    pc0 = torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev)
+                    ps0 = torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)
+                    K.kvq_encode_keys(pcb, None, keys, pc0, ps0)
+                    pcs.append((pc0, ps0))
+                else:
+                    pcs.append((pcs[0][0].clone(), pcs[0][1].clone()))
+
+            def pot_dec(i):
+                c, n = pcs[i % n_rot]
+                K.kvq_decode_attn(pcb, None, q, c, n, caches[i % n_rot][2], out=out, workspace=ws)
+
+            def pot_enc(i):
+                c, n = pcs[i % n_rot]
+                K.kvq_encode_keys(pcb, None, keys, c, n)
+
+            tag = "pot-m" if mant else "pot"
+            row(name, tag + "-decode", timed(pot_dec, n_rot), rd, B * Hq * T, B * Hkv * T)
+            row(name, tag + "-encode", timed(pot_enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
+            del pcs
+        del caches, keys, scores
         torch.cuda.empty_cache()
 
     # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes

@@ -790,3 +790,28 @@ def test_pot_scores_and_attention_equal_dequantized(oracle_mod, d, b, mant, G):
     lens = [T, 5]
     s2 = oracle_mod.pot_scores(q, codes, scales, b, mant, seq_lens=lens)
     assert np.all(np.isneginf(s2[1, :, 5:])) and np.array_equal(s2[1, :, :5], s[1, :, :5])
+
+
+def test_pot_iso_bit_accuracy_on_long_context_keys(oracle_mod):
+    """At 4 bits per element on the long-context keys (Gaussian within a key, LogNormal(0, 0.5) key scales),
+    the mantissa term cuts the RMS score error well below the plain power-of-two code (the page reports
+    about half), and the rotated Lloyd-Max code is more accurate than both."""
+    sh = W.LONGCTX
+    q = W.queries(sh)[[0]].astype(np.float64)
+    k = W.keys(sh, batches=[0], T=512).astype(np.float64)
+    s_ex = np.einsum("bhd,bhtd->bht", q, np.repeat(k, sh.Hq // sh.Hkv, axis=1))
+
+    def rms(s):
+        return math.sqrt(((s - s_ex) ** 2).mean() / (s_ex ** 2).mean())
+
+    e = {}
+    for m in (0, 1):
+        c, a, _ = oracle_mod.pot_encode(k, 4, m)
+        e[m] = rms(oracle_mod.pot_scores(q, c, a, 4, m))
+    lv, th = oracle_mod.codebook(sh.d, 4)
+    sg = W.signs(sh)
+    c, n, _, _ = oracle_mod.encode_keys(th, sg, k, 4)
+    e_h = rms(oracle_mod.scores(lv, sg, q, c, n))
+    print("score rel RMS error: plain %.4f, mantissa %.4f, Hadamard/Lloyd-Max %.4f" % (e[0], e[1], e_h))
+    assert e[1] < 0.75 * e[0]
+    assert e_h < e[1]
