@@ -310,53 +310,57 @@ def kmeans(train, K: int, iters: int, init_rows):
     return cent, obj
 
 
-def pq_encode(cent, keys):
-    """PQ codes [..., m] of keys [..., d] for one head's centroids [m, K, d/m]; returns (codes, gap)."""
+def pq_encode(cent, keys, bits: int = 8):
+    """PQ codes [..., m*bits/8] of keys [..., d] for one head's centroids [m, K, d/m]; returns (codes, gap [..., m]).
+    bits = 8: one byte per subspace; bits = 4 (K <= 16): two subspaces per byte, the even one low."""
     cent = _f64(cent)
     m, K, ds = cent.shape
+    assert bits == 8 or (bits == 4 and K <= 16 and m % 2 == 0)
     keys = _f64(keys)
     d = keys.shape[-1]
     assert d == m * ds
     lead = keys.shape[:-1]
     n = int(np.prod(lead)) if lead else 1
-    codes = np.zeros((n, m), dtype=np.uint8)
+    bpk = m * bits // 8
+    codes = np.zeros((n, bpk), dtype=np.uint8)
     gap = np.zeros((n, m))
-    _load().ora_pq_encode(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), _p(cent), _p(keys),
+    _load().ora_pq_encode(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), ctypes.c_int(bits), _p(cent), _p(keys),
                           ctypes.c_int64(n), _p(codes), _p(gap))
-    return codes.reshape(lead + (m,)), gap.reshape(lead + (m,))
+    return codes.reshape(lead + (bpk,)), gap.reshape(lead + (m,))
 
 
-def pq_scores(cent, q, codes, seq_lens=None) -> np.ndarray:
-    """PQ-ADC scores [B, Hq, T]; cent [Hkv, m, K, d/m], q [B, Hq, d], codes [B, Hkv, T, m]."""
+def pq_scores(cent, q, codes, seq_lens=None, bits: int = 8) -> np.ndarray:
+    """PQ-ADC scores [B, Hq, T]; cent [Hkv, m, K, d/m], q [B, Hq, d], codes [B, Hkv, T, m*bits/8]."""
     cent = _f64(cent)
     Hkv, m, K, ds = cent.shape
     q = _f64(q)
     B, Hq, d = q.shape
     codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
     T = codes.shape[2]
-    assert codes.shape == (B, Hkv, T, m)
+    assert codes.shape == (B, Hkv, T, m * bits // 8)
     lens = _lens(seq_lens, B)
     out = np.zeros((B, Hq, T))
-    _load().ora_pq_scores(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), _p(cent), _p(q), _p(codes),
-                          ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int64(T),
+    _load().ora_pq_scores(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), ctypes.c_int(bits), _p(cent), _p(q),
+                          _p(codes), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int64(T),
                           None if lens is None else _p(lens), _p(out))
     return out
 
 
-def pq_decode_attn(cent, q, codes, v, scale: float, seq_lens=None) -> np.ndarray:
+def pq_decode_attn(cent, q, codes, v, scale: float, seq_lens=None, bits: int = 8) -> np.ndarray:
     cent = _f64(cent)
     Hkv, m, K, ds = cent.shape
     q = _f64(q)
     B, Hq, d = q.shape
     codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
     T = codes.shape[2]
+    assert codes.shape == (B, Hkv, T, m * bits // 8)
     v = _f64(v)
     assert v.shape == (B, Hkv, T, d)
     lens = _lens(seq_lens, B)
     out = np.zeros((B, Hq, d))
-    _load().ora_pq_decode_attn(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), _p(cent), _p(q), _p(codes),
-                               _p(v), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv), ctypes.c_int64(T),
-                               None if lens is None else _p(lens), ctypes.c_double(scale), _p(out))
+    _load().ora_pq_decode_attn(ctypes.c_int(d), ctypes.c_int(m), ctypes.c_int(K), ctypes.c_int(bits), _p(cent),
+                               _p(q), _p(codes), _p(v), ctypes.c_int(B), ctypes.c_int(Hq), ctypes.c_int(Hkv),
+                               ctypes.c_int64(T), None if lens is None else _p(lens), ctypes.c_double(scale), _p(out))
     return out
 
 

@@ -537,24 +537,33 @@ void ora_kmeans(const double* train, int64_t n, int ds, int K, int iters, const 
 }
 
 /* PQ encode of n keys [n][d] for one head: code_s = nearest centroid of
- * sub-vector s.  cent [m][K][d/m]; codes [n][m]; gap (may be NULL) [n][m]. */
-void ora_pq_encode(int d, int m, int K, const double* cent, const double* keys, int64_t n,
+ * sub-vector s.  cent [m][K][d/m]; codes [n][m*cbits/8]: code s in bits
+ * [s*cbits, s*cbits+cbits) of the key's row, LSB first (cbits = 8: one byte
+ * per subspace; cbits = 4, for K <= 16: two subspaces per byte, the even one
+ * in the low nibble); gap (may be NULL) [n][m]. */
+void ora_pq_encode(int d, int m, int K, int cbits, const double* cent, const double* keys, int64_t n,
                    uint8_t* codes, double* gap) {
   const int ds = d / m;
-  for (int64_t r = 0; r < n; ++r)
+  const int bpk = m * cbits / 8;
+  for (int64_t r = 0; r < n; ++r) {
+    uint8_t* row = codes + (size_t)r * bpk;
+    memset(row, 0, (size_t)bpk);
     for (int s = 0; s < m; ++s) {
       double g;
       int c = nearest(keys + (size_t)r * d + (size_t)s * ds, cent + (size_t)s * K * ds, K, ds, &g);
-      codes[(size_t)r * m + s] = (uint8_t)c;
+      put_code(row, s, cbits, c);
       if (gap) gap[(size_t)r * m + s] = g;
     }
+  }
 }
 
 /* PQ scores [B][Hq][Tcap]: LUT[s][c] = q_s . C_{s,c}, score = sum_s LUT[s][code_s].
- * cent [Hkv][m][K][d/m]; codes [B][Hkv][Tcap][m].  No rotation, no norm. */
-void ora_pq_scores(int d, int m, int K, const double* cent, const double* q, const uint8_t* codes,
+ * cent [Hkv][m][K][d/m]; codes [B][Hkv][Tcap][m*cbits/8] as ora_pq_encode
+ * writes them.  No rotation, no norm. */
+void ora_pq_scores(int d, int m, int K, int cbits, const double* cent, const double* q, const uint8_t* codes,
                    int B, int Hq, int Hkv, int64_t Tcap, const int32_t* seq_lens, double* scores) {
   const int ds = d / m;
+  const int bpk = m * cbits / 8;
   const int G = Hq / Hkv;
   double* lut = (double*)malloc(sizeof(double) * (size_t)m * K);
   for (int bi = 0; bi < B; ++bi) {
@@ -572,9 +581,9 @@ void ora_pq_scores(int d, int m, int K, const double* cent, const double* q, con
       double* srow = scores + ((size_t)bi * Hq + h) * Tcap;
       for (int64_t t = 0; t < Tcap; ++t) {
         if (t >= len) { srow[t] = -INFINITY; continue; }
-        const uint8_t* row = codes + (((size_t)bi * Hkv + kvh) * Tcap + t) * m;
+        const uint8_t* row = codes + (((size_t)bi * Hkv + kvh) * Tcap + t) * bpk;
         double acc = 0.0;
-        for (int s = 0; s < m; ++s) acc += lut[(size_t)s * K + row[s]];
+        for (int s = 0; s < m; ++s) acc += lut[(size_t)s * K + get_code(row, s, cbits)];
         srow[t] = acc;
       }
     }
@@ -583,12 +592,12 @@ void ora_pq_scores(int d, int m, int K, const double* cent, const double* q, con
 }
 
 /* PQ decode attention: softmax(scale * PQ scores) . V. */
-void ora_pq_decode_attn(int d, int m, int K, const double* cent, const double* q, const uint8_t* codes,
+void ora_pq_decode_attn(int d, int m, int K, int cbits, const double* cent, const double* q, const uint8_t* codes,
                         const double* v, int B, int Hq, int Hkv, int64_t Tcap, const int32_t* seq_lens,
                         double scale, double* out) {
   const int G = Hq / Hkv;
   double* s = (double*)malloc(sizeof(double) * (size_t)B * Hq * (Tcap > 0 ? Tcap : 1));
-  ora_pq_scores(d, m, K, cent, q, codes, B, Hq, Hkv, Tcap, seq_lens, s);
+  ora_pq_scores(d, m, K, cbits, cent, q, codes, B, Hq, Hkv, Tcap, seq_lens, s);
   for (int bi = 0; bi < B; ++bi) {
     const int64_t len = seq_len_of(seq_lens, bi, Tcap);
     for (int h = 0; h < Hq; ++h) {

@@ -514,6 +514,32 @@ def test_pq_scores_and_attention_equal_dequantized(oracle_mod):
     np.testing.assert_allclose(out, _torch_sdpa(q, khat, v, 0.125, 1), rtol=1e-10, atol=1e-12)
 
 
+def test_pq_4bit_codes_pack_two_subspaces_per_byte(oracle_mod):
+    """With K <= 16 centroids the code of subspace s sits in nibble s of the row (even subspaces low):
+    byte j = idx[2j] | idx[2j+1] << 4 with idx the brute-force nearest centroids; scores and attention read
+    the same indices as the one-byte layout."""
+    rng = np.random.default_rng(12)
+    d, m, K = 64, 4, 16
+    B, H, T = 2, 2, 30
+    cent = rng.standard_normal((H, m, K, d // m))
+    keys = rng.standard_normal((B, H, T, d))
+    q = rng.standard_normal((B, H, d))
+    v = rng.standard_normal((B, H, T, d))
+    c8 = np.zeros((B, H, T, m), dtype=np.uint8)
+    c4 = np.zeros((B, H, T, m // 2), dtype=np.uint8)
+    for h in range(H):
+        c8[:, h] = oracle_mod.pq_encode(cent[h], keys[:, h])[0]
+        c4[:, h] = oracle_mod.pq_encode(cent[h], keys[:, h], bits=4)[0]
+    for s in range(m):
+        sub = keys[..., s * 16:(s + 1) * 16]
+        dist = ((sub[..., None, :] - cent[None, :, s, None, :, :]) ** 2).sum(-1)  # [B, H, T, K]
+        np.testing.assert_array_equal(c8[..., s], np.argmin(dist, axis=-1))
+    np.testing.assert_array_equal(c4, c8[..., 0::2] | (c8[..., 1::2] << 4))
+    np.testing.assert_array_equal(oracle_mod.pq_scores(cent, q, c4, bits=4), oracle_mod.pq_scores(cent, q, c8))
+    np.testing.assert_array_equal(oracle_mod.pq_decode_attn(cent, q, c4, v, 0.125, bits=4),
+                                  oracle_mod.pq_decode_attn(cent, q, c8, v, 0.125))
+
+
 # ----------------------------------------------------------------------------------------------
 # Workload generators: seeded and reproducible per batch slice
 # ----------------------------------------------------------------------------------------------
