@@ -294,39 +294,41 @@ def run_suite(K, torch, reps=5, calls=30):
         del caches, keys, scores
         torch.cuda.empty_cache()
 
-    # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes
-    sh = W.PQ_GPT2
-    B, H, d, T, m, Kc = sh.B, sh.Hq, sh.d, sh.T, sh.m, sh.K
-    cent = rnd(H, m, Kc, d // m)
-    cb = K.kvq_codebook_pq(d, m, Kc, H, cent)
-    n_rot = 8
-    keys = rnd(B, H, T, d).half()
-    codes0 = torch.empty((B, H, T, m), dtype=torch.uint8, device=dev)
-    K.kvq_encode_keys(cb, None, keys, codes0)
-    vals = rnd(B, H, T, d).half()
-    caches = [(codes0, vals)] + [(codes0.clone(), vals.clone()) for _ in range(n_rot - 1)]
-    q = rnd(B, H, d).half()
-    out = torch.empty((B, H, d), dtype=torch.float16, device=dev)
-    ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, H, H, T, 0), 16), dtype=torch.uint8, device=dev)
-    scores = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes: byte codes (K = 256) and
+    # 4-bit codes (K = 16, two subspaces per byte) at 32x and 64x compression
+    for sh in (W.PQ_GPT2, W.PQ4_GPT2_32X, W.PQ4_GPT2_64X):
+        B, H, d, T, m, Kc = sh.B, sh.Hq, sh.d, sh.T, sh.m, sh.K
+        cent = rnd(H, m, Kc, d // m)
+        cb = K.kvq_codebook_pq(d, m, Kc, H, cent)
+        bpk = cb.bytes_per_key
+        n_rot = 8
+        keys = rnd(B, H, T, d).half()
+        codes0 = torch.empty((B, H, T, bpk), dtype=torch.uint8, device=dev)
+        K.kvq_encode_keys(cb, None, keys, codes0)
+        vals = rnd(B, H, T, d).half()
+        caches = [(codes0, vals)] + [(codes0.clone(), vals.clone()) for _ in range(n_rot - 1)]
+        q = rnd(B, H, d).half()
+        out = torch.empty((B, H, d), dtype=torch.float16, device=dev)
+        ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, H, H, T, 0), 16), dtype=torch.uint8, device=dev)
+        scores = torch.empty((B, H, T), dtype=torch.float32, device=dev)
 
-    def pq_dec(i):
-        c, v = caches[i % n_rot]
-        K.kvq_decode_attn(cb, None, q, c, None, v, out=out, workspace=ws)
+        def pq_dec(i):
+            c, v = caches[i % n_rot]
+            K.kvq_decode_attn(cb, None, q, c, None, v, out=out, workspace=ws)
 
-    def pq_score(i):
-        c, _ = caches[i % n_rot]
-        K.kvq_score(cb, None, q, c, None, scores=scores)
+        def pq_score(i):
+            c, _ = caches[i % n_rot]
+            K.kvq_score(cb, None, q, c, None, scores=scores)
 
-    def pq_enc(i):
-        c, _ = caches[i % n_rot]
-        K.kvq_encode_keys(cb, None, keys, c)
+        def pq_enc(i):
+            c, _ = caches[i % n_rot]
+            K.kvq_encode_keys(cb, None, keys, c)
 
-    nkeys = B * H * T
-    row("pq_gpt2", "decode", timed(pq_dec, n_rot), nkeys * (m + 2 * d) + B * H * d * 2, nkeys, nkeys)
-    row("pq_gpt2", "score", timed(pq_score, n_rot), nkeys * (m + 4), nkeys, nkeys)
-    row("pq_gpt2", "encode", timed(pq_enc, n_rot), nkeys * (2 * d + m), 0, nkeys)
-    del caches, keys, vals
+        nkeys = B * H * T
+        row(sh.name, "decode", timed(pq_dec, n_rot), nkeys * (bpk + 2 * d) + B * H * d * 2, nkeys, nkeys)
+        row(sh.name, "score", timed(pq_score, n_rot), nkeys * (bpk + 4), nkeys, nkeys)
+        row(sh.name, "encode", timed(pq_enc, n_rot), nkeys * (2 * d + bpk), 0, nkeys)
+        del caches, keys, vals
     torch.cuda.empty_cache()
 
     # one-time sign-pattern selection: 200 candidates on 8 calibration samples of 512 keys.  The call is

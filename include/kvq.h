@@ -80,7 +80,9 @@ typedef enum kvq_kind {
 typedef struct kvq_codebook {
   int32_t kind;                            /* kvq_kind */
   int32_t d;                               /* head dimension */
-  int32_t b;                               /* HLM: bits per coordinate, 1..4; POT: bits per element, 2..4 */
+  int32_t b;                               /* HLM: bits per coordinate, 1..4; POT: bits per element, 2..4;
+                                              PQ: bits per subspace code, 8 or 4 (K <= 16, m even: two
+                                              codes per byte, the even subspace in the low nibble) */
   int32_t m;                               /* PQ: number of subspaces (d % m == 0); POT: 1 with the mantissa term */
   int32_t K;                               /* PQ: centroids per subspace, 2..256 */
   int32_t n_heads;                         /* PQ: kv heads covered by pq_centroids */
@@ -137,7 +139,10 @@ kvq_status kvq_build_codebook_pot(int d, int b, int mantissa, kvq_codebook* out)
 
 /* Fill a KVQ_PQ codebook that refers to device centroids
  * [n_heads][m][K][d/m] fp32 (caller-owned; must outlive every call using
- * the codebook).  Host only. */
+ * the codebook).  Host only.  The code width b is set to 4 when K <= 16 and m
+ * is even (LOOKAT's 32x and 64x compressions at d = 64 are m = 8 and m = 4
+ * with K = 16), else 8; a caller may set b = 8 afterwards to keep one byte per
+ * subspace. */
 kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centroids_device, kvq_codebook* out);
 
 /* Write path: encode keys into the code cache (AXELRAM, Abstract: transform on
@@ -145,7 +150,7 @@ kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centro
  *   cb:        codebook (HLM, POT or PQ).
  *   signs:     host [d] int8, each +1 or -1 (HLM); ignored for POT and PQ (may be NULL).
  *   keys:      device [B][Hkv][T_new][d], dtype kdtype (may be NULL when T_new == 0).
- *   codes:     device [B][Hkv][T_cap][d*b/8] (HLM) or [B][Hkv][T_cap][m] (PQ)
+ *   codes:     device [B][Hkv][T_cap][d*b/8] (HLM, POT) or [B][Hkv][T_cap][m*b/8] (PQ)
  *              uint8; rows pos_b .. pos_b+T_new-1 of every (b, h) are written.
  *   norms:     device [B][Hkv][T_cap] fp32, same rows written (HLM);
  *              ignored for PQ (may be NULL).

@@ -59,6 +59,8 @@ kvq_status check_codebook(const kvq_codebook* cb) {
     if (cb->d <= 0 || cb->m <= 0 || cb->d % cb->m != 0)
       return fail(KVQ_ERR_INVALID_ARG, "PQ d=%d, m=%d: m must divide d", cb->d, cb->m);
     if (cb->K < 2 || cb->K > 256) return fail(KVQ_ERR_INVALID_ARG, "PQ K=%d: must be 2..256", cb->K);
+    if (cb->b != 8 && !(cb->b == 4 && cb->K <= 16 && cb->m % 2 == 0))
+      return fail(KVQ_ERR_INVALID_ARG, "PQ code width b=%d: must be 8, or 4 with K <= 16 and an even m", cb->b);
     if (!cb->pq_centroids) return fail(KVQ_ERR_INVALID_ARG, "PQ centroids pointer is NULL");
     if (!aligned16(cb->pq_centroids)) return fail(KVQ_ERR_INVALID_ARG, "PQ centroids not 16-byte aligned");
     if (cb->n_heads <= 0) return fail(KVQ_ERR_INVALID_ARG, "PQ n_heads=%d", cb->n_heads);
@@ -67,7 +69,7 @@ kvq_status check_codebook(const kvq_codebook* cb) {
   return fail(KVQ_ERR_INVALID_ARG, "unknown codebook kind %d", cb->kind);
 }
 
-int bytes_per_key(const kvq_codebook* cb) { return cb->kind == KVQ_PQ ? cb->m : cb->d * cb->b / 8; }
+int bytes_per_key(const kvq_codebook* cb) { return cb->kind == KVQ_PQ ? cb->m * cb->b / 8 : cb->d * cb->b / 8; }
 
 kvq_status pack_signs(const int8_t* signs, int d, uint32_t out[8]) {
   for (int k = 0; k < 8; ++k) out[k] = 0;
@@ -256,6 +258,7 @@ kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centro
   out->d = d;
   out->m = m;
   out->K = K;
+  out->b = K <= 16 && m % 2 == 0 ? 4 : 8;  // the narrowest code width that holds K centroids
   out->n_heads = n_heads;
   out->pq_centroids = centroids_device;
   kvq_status st = check_codebook(out);
@@ -319,7 +322,7 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
   p.pq_cent = cb->pq_centroids;
   p.pq_K = cb->K;
   if (T_new == 0) return ok();
-  return from_hip(kvq::launch_pq_encode(cb->d, cb->m, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
+  return from_hip(kvq::launch_pq_encode(cb->d, cb->m, cb->b, kdtype == KVQ_F16, p, s), "kvq_encode_keys");
 }
 
 kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
@@ -337,7 +340,7 @@ kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cb->kind == KVQ_HADAMARD_LM) return from_hip(kvq::launch_hlm_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");
   if (cb->kind == KVQ_POT) return from_hip(kvq::launch_pot_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");
-  return from_hip(kvq::launch_pq_score(cb->d, cb->m, rs.gg, p, grid, s), "kvq_score");
+  return from_hip(kvq::launch_pq_score(cb->d, cb->m, cb->b, rs.gg, p, grid, s), "kvq_score");
 }
 
 size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv, int64_t T_cap, int n_splits) {
@@ -401,7 +404,7 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = cb->kind == KVQ_HADAMARD_LM ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
                  : cb->kind == KVQ_POT      ? kvq::launch_pot_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)
-                                            : kvq::launch_pq_decode(cb->d, cb->m, rs.gg, vdtype == KVQ_F16, p, grid, s);
+                                            : kvq::launch_pq_decode(cb->d, cb->m, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s);
   return from_hip(e, name);
 }
 

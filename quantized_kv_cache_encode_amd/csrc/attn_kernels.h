@@ -146,22 +146,26 @@ struct PotScorer : ScalarTable<D_, BITS> {
   static constexpr bool kRotate = false;
 };
 
-// Scorer for product quantization: rows = subspaces, cols = centroids (<= 256).
-template <int D_, int M>
+// Scorer for product quantization: rows = subspaces, cols = centroids.  CB = 8: one byte per subspace
+// (K <= 256); CB = 4: two subspaces per byte, the even one in the low nibble (K <= 16), so a row holds 16
+// entries and the gathers of a wave stay within one row like the scalar codecs' (no bank conflicts).
+template <int D_, int M, int CB = 8>
 struct PqScorer {
+  static_assert(CB == 8 || (CB == 4 && M % 2 == 0), "4-bit codes pair up subspaces");
   static constexpr int D = D_;
   static constexpr int ROWS = M;
-  static constexpr int COLS = 256;
-  static constexpr int CODE_BITS = 8;
-  static constexpr int BPK = M;
+  static constexpr int COLS = 1 << CB;
+  static constexpr int CODE_BITS = CB;
+  static constexpr int BPK = M * CB / 8;
   static constexpr int NW = (BPK + 3) / 4;
   static constexpr int DS = D / M;
   static constexpr bool kRotate = false;
   static constexpr bool kNorm = false;
-  static constexpr bool kNibbles = false;
+  static constexpr bool kNibbles = CB == 4;
   static constexpr bool kIntLut = false;
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) {
-    return (w[i >> 2] >> (8 * (i & 3))) & 255u;
+    if constexpr (CB == 4) return (w[i >> 3] >> (4 * (i & 7))) & 15u;
+    else return (w[i >> 2] >> (8 * (i & 3))) & 255u;
   }
   __device__ static __forceinline__ float level_max(const float*) { return 1.0f; }
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).

@@ -86,15 +86,16 @@ hipError_t launch_hlm_decode(int D, int bits, int heads_per_wg, bool v_f16, cons
                              hipStream_t s);
 hipError_t launch_hlm_score(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_hlm_decode_qv(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
-hipError_t launch_pq_decode(int D, int M, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
+// PQ launchers take the code width cb: 8 (one byte per subspace) or 4 (two subspaces per byte).
+hipError_t launch_pq_decode(int D, int M, int cb, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
                             hipStream_t s);
-hipError_t launch_pq_score(int D, int M, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_pq_score(int D, int M, int cb, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_hlm_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
 hipError_t launch_pot_decode(int D, int bits, int heads_per_wg, bool v_f16, const AttnParams& p, dim3 grid,
                              hipStream_t s);
 hipError_t launch_pot_score(int D, int bits, int heads_per_wg, const AttnParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_pot_encode(int D, int bits, bool k_f16, const EncodeParams& p, hipStream_t s);
-hipError_t launch_pq_encode(int D, int M, bool k_f16, const EncodeParams& p, hipStream_t s);
+hipError_t launch_pq_encode(int D, int M, int cb, bool k_f16, const EncodeParams& p, hipStream_t s);
 
 // Exact attention over calibration samples (sign-pattern selection).
 constexpr int kCalibMaxT = 8192;  // keys per calibration sample (scores held in LDS)

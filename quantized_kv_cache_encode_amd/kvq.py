@@ -54,7 +54,7 @@ class kvq_codebook(ctypes.Structure):
 
     @property
     def bytes_per_key(self) -> int:
-        return self.m if self.kind == KVQ_PQ else self.d * self.b // 8
+        return self.m * self.b // 8 if self.kind == KVQ_PQ else self.d * self.b // 8
 
 
 if not os.path.exists(LIB_PATH):

@@ -286,3 +286,17 @@ def test_pot_validation(K):
                                       None) == K.KVQ_ERR_UNSUPPORTED
     assert lib.kvq_decode_attn_qv(ctypes.byref(cb), None, P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1, 4, 2,
                                   128, None, 0.125, P(FAKE), 1, P(FAKE), 1 << 20, 0, None) == K.KVQ_ERR_UNSUPPORTED
+
+
+def test_pq_code_width(K):
+    P = ctypes.c_void_p
+    cb = K.kvq_codebook()
+    K._check(K._lib.kvq_codebook_pq(64, 8, 16, 2, P(FAKE), ctypes.byref(cb)))
+    assert cb.b == 4 and cb.bytes_per_key == 4
+    K._check(K._lib.kvq_codebook_pq(64, 8, 17, 2, P(FAKE), ctypes.byref(cb)))
+    assert cb.b == 8 and cb.bytes_per_key == 8
+    K._check(K._lib.kvq_codebook_pq(64, 4, 16, 2, P(FAKE), ctypes.byref(cb)))
+    assert cb.b == 4 and cb.bytes_per_key == 2
+    cb.K = 32  # 4-bit codes cannot index 32 centroids
+    assert _call_encode(K, cb, None, norms=None) == K.KVQ_ERR_INVALID_ARG
+    assert "code width" in K.kvq_last_error()

@@ -372,3 +372,76 @@ def test_pq_score_and_decode_parity(K, oracle_mod, pq_case):
     log("  PQ decode max rel L2 %.3g" % float(err.max()))
     assert np.all(err <= OUT_TOL)
     assert np.all(out[1] == 0)
+
+
+@pytest.fixture(scope="module", params=[W.PQ4_GPT2_32X, W.PQ4_GPT2_64X], ids=["pq4_32x", "pq4_64x"])
+def pq4_case(request, oracle_mod):
+    """4-bit centroid indices (K = 16), two subspaces per byte: centroids from the oracle's k-means, codes
+    from the oracle's encode."""
+    shape = request.param
+    train = W.pq_training(shape)
+    start = W.pq_start_rows(shape)
+    ds = shape.d // shape.m
+    cent = np.zeros((shape.Hkv, shape.m, shape.K, ds))
+    for h in range(shape.Hkv):
+        for s in range(shape.m):
+            cent[h, s], _ = oracle_mod.kmeans(train[h][:, s * ds:(s + 1) * ds], shape.K, 10, start[h, s])
+    cent32 = cent.astype(np.float32)
+    keys = W.keys(shape)
+    codes = np.zeros((shape.B, shape.Hkv, shape.T, shape.m // 2), dtype=np.uint8)
+    gaps = np.zeros((shape.B, shape.Hkv, shape.T, shape.m))
+    for h in range(shape.Hkv):
+        codes[:, h], gaps[:, h] = oracle_mod.pq_encode(cent32[h].astype(np.float64), keys[:, h], bits=4)
+    return dict(shape=shape, cent=cent32, q=W.queries(shape), keys=keys, v=W.values(shape), codes=codes, gaps=gaps)
+
+
+def test_pq4_encode_parity(K, oracle_mod, pq4_case):
+    import torch
+    sh = pq4_case["shape"]
+    cb = K.kvq_codebook_pq(sh.d, sh.m, sh.K, sh.Hkv, torch_dev(pq4_case["cent"]))
+    assert cb.b == 4 and cb.bytes_per_key == sh.m // 2
+    codes = torch.zeros((sh.B, sh.Hkv, sh.T, sh.m // 2), dtype=torch.uint8, device="cuda:0")
+    K.kvq_encode_keys(cb, None, torch_dev(pq4_case["keys"]), codes)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    gi = np.stack([got & 15, got >> 4], axis=-1).reshape(got.shape[:3] + (sh.m,))
+    ref = pq4_case["codes"]
+    ri = np.stack([ref & 15, ref >> 4], axis=-1).reshape(ref.shape[:3] + (sh.m,))
+    diff = np.argwhere(gi != ri)
+    log("  4-bit PQ codes differing: %d of %d" % (len(diff), gi.size))
+    ds = sh.d // sh.m
+    for b, h, t, s in diff:
+        x = pq4_case["keys"][b, h, t, s * ds:(s + 1) * ds].astype(np.float64)
+        c = pq4_case["cent"][h, s].astype(np.float64)
+        dist = ((x[None, :] - c) ** 2).sum(-1)
+        assert dist[gi[b, h, t, s]] - dist[ri[b, h, t, s]] <= 4e-6 * dist[gi[b, h, t, s]] + 1e-12
+    assert len(diff) <= 1e-4 * gi.size
+
+
+def test_pq4_score_and_decode_parity(K, oracle_mod, pq4_case):
+    import torch
+    sh = pq4_case["shape"]
+    cb = K.kvq_codebook_pq(sh.d, sh.m, sh.K, sh.Hkv, torch_dev(pq4_case["cent"]))
+    codes = torch_dev(pq4_case["codes"])
+    qd = torch_dev(pq4_case["q"])
+    cent64 = pq4_case["cent"].astype(np.float64)
+    got = K.kvq_score(cb, None, qd, codes).cpu().numpy()
+    ref = oracle_mod.pq_scores(cent64, pq4_case["q"], pq4_case["codes"], bits=4)
+    c = pq4_case["codes"]
+    idx = np.stack([c & 15, c >> 4], axis=-1).reshape(c.shape[:3] + (sh.m,))
+    khat_norm = np.zeros(c.shape[:3])
+    for h in range(sh.Hkv):
+        for s in range(sh.m):
+            khat_norm[:, h] += (cent64[h, s][idx[:, h, :, s]] ** 2).sum(-1)
+    tol = 1e-4 * np.linalg.norm(pq4_case["q"].astype(np.float64), axis=-1)[:, :, None] * np.sqrt(khat_norm)
+    assert np.all(np.abs(got - ref) <= tol)
+    lens = [1024, 0, 700, 1]
+    out = K.kvq_decode_attn(cb, None, qd, codes, None, torch_dev(pq4_case["v"]), scale=scale_of(sh.d),
+                            seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
+                            out_dtype=torch.float32).cpu().numpy()
+    refo = oracle_mod.pq_decode_attn(cent64, pq4_case["q"], pq4_case["codes"], pq4_case["v"], scale_of(sh.d),
+                                     seq_lens=lens, bits=4)
+    err = rel_l2_rows(out, refo)
+    log("  4-bit PQ decode max rel L2 %.3g" % float(err.max()))
+    assert np.all(err <= OUT_TOL)
+    assert np.all(out[1] == 0)

@@ -68,6 +68,10 @@ LLAMA8B = Shape("llama8b", B=1, Hq=32, Hkv=8, d=128, T=4096, b=4, key_scale="cha
 LONGCTX = Shape("longctx", B=8, Hq=32, Hkv=4, d=64, T=32768, b=4, key_scale="token_lognormal",
                 seed=SEED_BASE + 2)
 PQ_GPT2 = Shape("pq_gpt2", B=4, Hq=12, Hkv=12, d=64, T=1024, m=8, K=256, seed=SEED_BASE + 4)
+# 4-bit centroid indices (K = 16) at the same shapes: 4 B per key (m = 8, 32x smaller than fp16 keys) and
+# 2 B per key (m = 4, 64x), the two compressions LOOKAT's abstract reports
+PQ4_GPT2_32X = Shape("pq4_gpt2_32x", B=4, Hq=12, Hkv=12, d=64, T=1024, m=8, K=16, seed=SEED_BASE + 4)
+PQ4_GPT2_64X = Shape("pq4_gpt2_64x", B=4, Hq=12, Hkv=12, d=64, T=1024, m=4, K=16, seed=SEED_BASE + 4)
 SIGNSEL = Shape("signsel", B=8, Hq=32, Hkv=8, d=128, T=512, b=4, key_scale="channel_lognormal",
                 v_scale="channel_lognormal", seed=SEED_BASE + 5)
 SIGN_CANDIDATES = 200
