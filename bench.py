@@ -377,7 +377,7 @@ def main(argv=None):
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (got --gpus %d)" % a.gpus)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (got --gpus %d)" % a.gpus)
         return 2
 
     import numpy as np
