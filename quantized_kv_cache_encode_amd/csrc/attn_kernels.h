@@ -594,10 +594,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   Chunk ka, kb;
 
   // Fused append (Hadamard/Lloyd-Max codec): the workgroup whose split holds the sequence's last position
-  // encodes the new key itself -- wave 1, D/8 lanes, with the arithmetic of the encode kernel -- keeps its
+  // encodes the new key itself -- wave 1, D/16 lanes, with the arithmetic of the encode kernel -- keeps its
   // codes and norm in LDS for its own scores, and (head group 0 only) writes them to the cache.  Every
   // wave issues the key load; it reads zeros except in the encoding lanes, so it needs no branch.
-  constexpr int LPK = D / 8;
+  constexpr int LPK = EncLanes<D>::LPK;
   const bool app = S::kRotate && p.new_keys != nullptr && n_valid > 0 && u.len <= t_begin + p.split_len;
   const int rel = n_valid - 1;  // the new key's position within the split, when app
   const bool enc_lanes = app && wid == 1 && lane < LPK;
@@ -606,30 +606,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(app ? (const void*)(reinterpret_cast<const char*>(p.new_keys) + new_row * D * kesz) : p.codes,
                 app && wid == 1 ? D * kesz : 0);
-  uint32_t kraw[8];
+  uint32_t kraw[kEncCpl];  // the lane's 16 coordinates of the new key (fp16 in the first 8 words)
 
   // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
   // burst streams in while the queries are rotated and the table is built.
   prologue<S, GG>(p, u, qs, qa, lv, tid, [&] {
     fetch_codes(c, ka);
     fetch_v(c, ka);
-    const int ko = lane * 8 * kesz;
-    const auto r0 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0);
-    const auto r1 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16, 0, 0);
+    const int ko = lane * kEncCpl * kesz;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kraw[j] = r0[j];
-      kraw[4 + j] = r1[j];
+    for (int h = 0; h < kEncCpl / 4; ++h) {  // fp32: four 16-byte loads; fp16: two, the rest read zeros
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
     }
   });
   if constexpr (S::kRotate) {
     if (enc_lanes) {
-      float x[8];
+      float x[kEncCpl];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < kEncCpl; ++j)
         x[j] = p.new_f16 ? h2f((uint16_t)(kraw[j / 2] >> (16 * (j % 2)))) : __builtin_bit_cast(float, kraw[j]);
       float nrm;
-      const uint32_t packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
+      const uint64_t packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
       store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
       if (lane == 0) *s_newn = nrm;
       if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)

@@ -6,13 +6,13 @@
 // Walsh-Hadamard matrix and D the sign pattern, code_i = #{ j : t_j <= y_i },
 // codes packed LSB-first (b bits per coordinate) next to the fp32 norm.
 //
-// Layout: 8 coordinates per lane, D/8 lanes per key, so a wave holds 64/(D/8)
-// keys.  The key is read with one 16-byte load per lane (fp16) and fully
-// coalesced across the wave.  The transform is an in-register radix-2 fast
-// Walsh-Hadamard transform for the lane's 8 coordinates followed by
-// log2(D/8) cross-lane butterfly stages; ||k||^2 is reduced across the same
-// lanes.  Each lane then compares its 8 coordinates with the thresholds,
-// packs 8*b bits and stores them at its own byte offset of the key's row.
+// Layout: 16 coordinates per lane, D/16 lanes per key, so a wave holds
+// 64/(D/16) keys.  The key is read with two 16-byte loads per lane (fp16) and
+// fully coalesced across the wave.  The transform is an in-register radix-2
+// fast Walsh-Hadamard transform for the lane's 16 coordinates followed by
+// log2(D/16) cross-lane butterfly stages; ||k||^2 is reduced across the same
+// lanes.  Each lane then finds the codes of its 16 coordinates, packs 16*b
+// bits and stores them at its own byte offset of the key's row.
 #include "encode_dev.h"
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -21,7 +21,7 @@ namespace kvq {
 
 template <int D, int BITS, bool KF16>
 __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
-  constexpr int LPK = D / 8;           // lanes per key
+  constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
   constexpr int KPB = 256 / LPK;       // keys per workgroup per pass
   constexpr int BPK = D * BITS / 8;    // code bytes per key
   constexpr int L = 1 << BITS;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
 
   const int tid = threadIdx.x;
   const int lk = tid & (LPK - 1);
-  float sg[8];
+  float sg[kEncCpl];
   lane_signs<D>(p.signs, lk, sg);
   const int64_t n_keys = p.key_end - p.key_begin;
   const int64_t stride = (int64_t)gridDim.x * KPB;
@@ -54,13 +54,13 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
       __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(reinterpret_cast<const char*>(p.keys) + p.key_begin * D * ESZ),
                                         0, (int)(n_keys * D * ESZ), 0x00020000);
   typedef unsigned u4 __attribute__((ext_vector_type(4)));
-  struct Raw { u4 a, b; };
+  constexpr int NV = kEncCpl * ESZ / 16;  // 16-byte loads per lane and key
+  struct Raw { u4 v[NV]; };
   auto fetch = [&](int64_t key) {
     Raw r;
-    const int off = (int)(key < n_keys ? key : n_keys) * D * ESZ + lk * 8 * ESZ;
-    r.a = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0);
-    if constexpr (!KF16) r.b = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16, 0, 0);
-    else r.b = u4{0, 0, 0, 0};
+    const int off = (int)(key < n_keys ? key : n_keys) * D * ESZ + lk * kEncCpl * ESZ;
+#pragma unroll
+    for (int h = 0; h < NV; ++h) r.v[h] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16 * h, 0, 0);
     return r;
   };
   const float cell_max = (float)(p.n_cells - 1);
@@ -78,26 +78,24 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
   // One key: convert its coordinates, put the fetch two passes ahead into the registers just freed (so two
   // fetches stay in flight), transform, quantize, store.  The loop alternates two register sets.
   auto step = [&](int64_t k, Raw& r) {
-    float x[8];
-    if constexpr (KF16) {
+    float x[kEncCpl];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[2 * j] = h2f((uint16_t)(r.a[j] & 0xffffu));
-        x[2 * j + 1] = h2f((uint16_t)(r.a[j] >> 16));
-      }
-    } else {
+    for (int h = 0; h < NV; ++h)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // the vector elements go through named scalars: bit-casting an element expression directly
         // read element 0 for every j with this compiler
-        const uint32_t lo = r.a[j], hi = r.b[j];
-        x[j] = __builtin_bit_cast(float, lo);
-        x[4 + j] = __builtin_bit_cast(float, hi);
+        const uint32_t w = r.v[h][j];
+        if constexpr (KF16) {
+          x[8 * h + 2 * j] = h2f((uint16_t)(w & 0xffffu));
+          x[8 * h + 2 * j + 1] = h2f((uint16_t)(w >> 16));
+        } else {
+          x[4 * h + j] = __builtin_bit_cast(float, w);
+        }
       }
-    }
     r = fetch(k + 2 * stride);
     const float nrm = rotate_key_lane<D>(x, lk, sg);
-    const uint32_t packed = pack_lane_codes<BITS>(x, unit_scale<D>(nrm), code_of);
+    const uint64_t packed = pack_lane_codes<BITS>(x, unit_scale<D>(nrm), code_of);
 
     const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
     const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
@@ -122,7 +120,7 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
 
 template <int D, int BITS>
 static hipError_t encode_launch(bool kf16, const EncodeParams& p0, hipStream_t s) {
-  constexpr int KPB = 256 / (D / 8);
+  constexpr int KPB = 256 / EncLanes<D>::LPK;
   const int64_t n_keys = (int64_t)p0.B * p0.Hkv * p0.T_new;
   // launches of at most 2^30 key bytes each (32-bit buffer offsets); a persistent grid of at most 2048
   // workgroups (eight per compute unit) walks the keys of a launch

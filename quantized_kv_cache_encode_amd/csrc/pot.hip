@@ -7,8 +7,8 @@
 // midpoint takes the larger magnitude) and the sign bit k_i < 0 above it; codes are packed LSB-first next
 // to alpha in the norms buffer.  No rotation.
 //
-// Layout: 8 elements per lane, D/8 lanes per key (a wave holds 64/(D/8) keys); alpha is reduced across the
-// key's lanes; each lane packs its 8*b bits and stores them at its own byte offset of the key's row.  For
+// Layout: 16 elements per lane, D/16 lanes per key (a wave holds 64/(D/16) keys); alpha is reduced across
+// the key's lanes; each lane packs its 16*b bits and stores them at its own byte offset of the key's row.  For
 // fp16 keys every comparison is exact in fp32 (alpha has 11 significant bits and a midpoint at most 3).
 #include "encode_dev.h"
 #include "kvq_device.h"
@@ -22,13 +22,12 @@ __device__ __forceinline__ float key_lanes_max(float v) {
   if constexpr (LPK >= 4) v = fmaxf(v, xor_lane<2>(v));
   if constexpr (LPK >= 8) v = fmaxf(v, xor_lane<4>(v));
   if constexpr (LPK >= 16) v = fmaxf(v, xor_lane<8>(v));
-  if constexpr (LPK >= 32) v = fmaxf(v, xor_lane<16>(v));
   return v;
 }
 
 template <int D, int BITS, bool KF16>
 __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
-  constexpr int LPK = D / 8;      // lanes per key
+  constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
   constexpr int KPB = 256 / LPK;  // keys per workgroup per pass
   constexpr int BPK = D * BITS / 8;
   constexpr int NM = 1 << (BITS - 1);  // magnitudes
@@ -38,25 +37,28 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t { return (__umulhi(n, magic) + n) >> shift; };
   // every lane of a key takes the same trip count, so the cross-lane reduction sees all of them
   for (int64_t k = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK; k < n_keys; k += stride) {
-    float x[8];
+    float x[kEncCpl];
     load_key_lane<D, KF16>(p.keys, p.key_begin + k, lk, x);
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    for (int j = 0; j < kEncCpl; ++j) amax = fmaxf(amax, fabsf(x[j]));
     const float alpha = key_lanes_max<LPK>(amax);
     float lim[NM - 1];
 #pragma unroll
     for (int m = 0; m < NM - 1; ++m) lim[m] = p.thresholds[m] * alpha;
-    uint32_t packed = 0;
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kEncCpl; ++j) {
       const float a = fabsf(x[j]);
       uint32_t c = 0;
 #pragma unroll
       for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
       if (x[j] < 0.0f) c |= 1u << (BITS - 1);
-      packed |= c << (BITS * j);
+      const int bit = BITS * j;
+      if (bit < 32) lo |= c << bit;
+      if (bit + BITS > 32) hi |= bit >= 32 ? c << (bit - 32) : c >> (32 - bit);
     }
+    const uint64_t packed = ((uint64_t)hi << 32) | lo;
     const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
     const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
     const uint32_t t = gk - bh * (uint32_t)p.T_new;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
 
 template <int D, int BITS>
 static hipError_t pot_launch(bool kf16, const EncodeParams& p0, hipStream_t s) {
-  constexpr int KPB = 256 / (D / 8);
+  constexpr int KPB = 256 / EncLanes<D>::LPK;
   EncodeParams p = p0;
   p.key_begin = 0;
   p.key_end = (int64_t)p0.B * p0.Hkv * p0.T_new;
