@@ -48,7 +48,7 @@ constexpr int kChunk = 64;
 constexpr float kLazyHeadroom = 8.0f;  // log2 of the largest probability allowed before rescaling
 constexpr int kMaxSplits = 256;        // T splits per (b, kv head, head group)
 constexpr int kRecPad = 4;             // split partial record = D accumulators + max + sum, padded to D + 4
-constexpr int kMergeTile = 16;         // splits whose partials the merging workgroup loads at once
+constexpr int kMergeTile = 32;         // splits whose partials the merging workgroup loads at once
 
 template <int B, int NW>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int i) {

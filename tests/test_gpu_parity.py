@@ -235,19 +235,23 @@ def test_decode_parity(K, oracle_mod, name, shape, batches, T, lens, n_splits, o
 
 def test_decode_same_result_for_every_split_count(K, oracle_mod):
     import torch
-    shape = W.scaled(W.LONGCTX, B=1, T=2048)
+    shape = W.scaled(W.LONGCTX, B=1, T=8192)
     case = make_hlm_case(shape)
     ref_codes, ref_norms, _ = oracle_cache(oracle_mod, shape, case["keys"], case["signs"])
     codes, norms = _upload_cache(ref_codes, ref_norms)
     cb = K.kvq_build_codebook(64, 4)
     outs = []
-    for ns in (1, 2, 3, 8, 32):
+    # up to 128 splits of 64 tokens: the merging workgroup reads the partials in tiles of 32 splits
+    for ns in (1, 2, 3, 8, 32, 33, 100, 128):
         outs.append(K.kvq_decode_attn(cb, case["signs"], torch_dev(case["q"]), codes, norms, torch_dev(case["v"]),
                                       out_dtype=torch.float32, n_splits=ns).cpu().numpy())
     # the probabilities enter the matrix cores as fp16 relative to each split's running maximum, so split
     # counts agree to fp16 rounding (~2^-11 relative), well inside the 2e-3 bar against the oracle
     for o in outs[1:]:
         assert np.max(rel_l2_rows(o, outs[0])) < 1e-3
+    lv, _ = oracle_mod.codebook(64, 4)
+    ref = oracle_mod.decode_attn(lv, case["signs"], case["q"], ref_codes, ref_norms, case["v"], scale_of(64))
+    assert np.max(rel_l2_rows(outs[-1], ref)) <= OUT_TOL
 
 
 def test_longctx_full_size_sampled(K, oracle_mod):
