@@ -91,6 +91,29 @@ def test_pot_encode_write_position_and_zero_key(K, oracle_mod):
     del torch
 
 
+def test_pot_encode_per_batch_write_positions(K, oracle_mod):
+    """write_pos[b] places batch b's new keys; rows outside [0, T_cap) are skipped."""
+    import torch
+    shape = W.scaled(W.LLAMA8B, B=3, T=40)
+    keys = _case(shape)["keys"]
+    cb = K.kvq_build_codebook_pot(shape.d, 3, 1)
+    T_cap = 100
+    wp = np.array([0, 70, 90], dtype=np.int32)  # batch 2's last 30 rows fall past T_cap
+    codes = torch.zeros((3, shape.Hkv, T_cap, cb.bytes_per_key), dtype=torch.uint8, device="cuda:0")
+    scales = torch.zeros((3, shape.Hkv, T_cap), dtype=torch.float32, device="cuda:0")
+    K.kvq_encode_keys(cb, None, torch_dev(keys), codes, scales, write_pos=torch_dev(wp))
+    torch.cuda.synchronize()
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    ref_c, ref_s, _ = oracle_mod.pot_encode(keys, 3, 1)
+    for b, w in enumerate(wp):
+        n = min(40, T_cap - w)
+        np.testing.assert_array_equal(got_c[b, :, w:w + n], ref_c[b, :, :n])
+        np.testing.assert_array_equal(got_s[b, :, w:w + n], ref_s[b, :, :n].astype(np.float32))
+        untouched = np.ones(T_cap, dtype=bool)
+        untouched[w:w + n] = False
+        assert not got_c[b][:, untouched].any() and not got_s[b][:, untouched].any()
+
+
 def _upload(ref_c, ref_s):
     return torch_dev(ref_c), torch_dev(ref_s.astype(np.float32))
 
