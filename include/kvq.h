@@ -226,7 +226,9 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
  *   codes, norms: the cache, read and written (rows len_b - 1).
  *   Every other argument as kvq_decode_attn, including the workspace (same
  *   size, from kvq_decode_attn_workspace).
- * Errors: as kvq_decode_attn; KVQ_ERR_UNSUPPORTED for a PQ or POT codebook. */
+ * Hadamard/Lloyd-Max and power-of-two codebooks (for the latter, norms holds
+ * the per-key scales and signs may be NULL).
+ * Errors: as kvq_decode_attn; KVQ_ERR_UNSUPPORTED for a PQ codebook. */
 kvq_status kvq_decode_attn_append(const kvq_codebook* cb, const int8_t* signs, const void* new_keys,
                                   kvq_dtype kdtype, const void* q, kvq_dtype qdtype, uint8_t* codes, float* norms,
                                   const void* v, kvq_dtype vdtype, int B, int Hq, int Hkv, int64_t T_cap,

@@ -375,15 +375,17 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
   if (n_splits < 0) return fail(KVQ_ERR_INVALID_ARG, "n_splits=%d", n_splits);
   if (!std::isfinite(scale)) return fail(KVQ_ERR_INVALID_ARG, "scale is not finite");
   if (new_keys) {
-    if (cb->kind != KVQ_HADAMARD_LM)
-      return fail(KVQ_ERR_UNSUPPORTED, "the fused append supports the Hadamard/Lloyd-Max codec only");
+    if (cb->kind == KVQ_PQ) return fail(KVQ_ERR_UNSUPPORTED, "the fused append supports the scalar codecs only");
     if (!valid_dtype(kdtype)) return fail(KVQ_ERR_INVALID_ARG, "bad key dtype %d", (int)kdtype);
     if (!aligned16(new_keys)) return fail(KVQ_ERR_INVALID_ARG, "new_keys not 16-byte aligned");
     p.new_keys = new_keys;
     p.new_f16 = kdtype == KVQ_F16;
     p.app_codes = const_cast<uint8_t*>(codes);
     p.app_norms = const_cast<float*>(norms);
-    for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
+    if (cb->kind == KVQ_POT)  // midpoints of the 2^(b-1) magnitudes
+      for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << (cb->b - 1)) ? cb->thresholds[j] : 0.0f;
+    else
+      for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
   }
   p.seq_lens = seq_lens;
   p.v = v;

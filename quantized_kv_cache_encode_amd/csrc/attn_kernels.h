@@ -593,12 +593,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   int c = wid * kChunk;  // chunk start, relative to t_begin
   Chunk ka, kb;
 
-  // Fused append (Hadamard/Lloyd-Max codec): the workgroup whose split holds the sequence's last position
+  // Fused append (the scalar codecs): the workgroup whose split holds the sequence's last position
   // encodes the new key itself -- wave 1, D/16 lanes, with the arithmetic of the encode kernel -- keeps its
   // codes and norm in LDS for its own scores, and (head group 0 only) writes them to the cache.  Every
   // wave issues the key load; it reads zeros except in the encoding lanes, so it needs no branch.
   constexpr int LPK = EncLanes<D>::LPK;
-  const bool app = S::kRotate && p.new_keys != nullptr && n_valid > 0 && u.len <= t_begin + p.split_len;
+  const bool app = S::kIntLut && p.new_keys != nullptr && n_valid > 0 && u.len <= t_begin + p.split_len;
   const int rel = n_valid - 1;  // the new key's position within the split, when app
   const bool enc_lanes = app && wid == 1 && lane < LPK;
   const int64_t new_row = (int64_t)u.b * p.Hkv + u.kvh;
@@ -621,14 +621,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
     }
   });
-  if constexpr (S::kRotate) {
+  if constexpr (S::kIntLut) {
     if (enc_lanes) {
       float x[kEncCpl];
 #pragma unroll
       for (int j = 0; j < kEncCpl; ++j)
         x[j] = p.new_f16 ? h2f((uint16_t)(kraw[j / 2] >> (16 * (j % 2)))) : __builtin_bit_cast(float, kraw[j]);
-      float nrm;
-      const uint64_t packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
+      float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
+      uint64_t packed;
+      if constexpr (S::kRotate) packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
+      else packed = pot_encode_lane<D, S::CODE_BITS>(x, p.thresholds, nrm);
       store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
       if (lane == 0) *s_newn = nrm;
       if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)

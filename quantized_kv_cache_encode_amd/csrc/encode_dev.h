@@ -44,6 +44,16 @@ __device__ __forceinline__ float key_lanes_sum(float v) {
   return v;
 }
 
+// Maximum of v over the LPK lanes of the key (the same value in all of them).
+template <int LPK>
+__device__ __forceinline__ float key_lanes_max(float v) {
+  if constexpr (LPK >= 2) v = fmaxf(v, xor_lane<1>(v));
+  if constexpr (LPK >= 4) v = fmaxf(v, xor_lane<2>(v));
+  if constexpr (LPK >= 8) v = fmaxf(v, xor_lane<4>(v));
+  if constexpr (LPK >= 16) v = fmaxf(v, xor_lane<8>(v));
+  return v;
+}
+
 // Sign of coordinate 16*lk + j under the pattern D (bit i of `signs` set: coordinate i negated), as +-1.
 template <int D>
 __device__ __forceinline__ void lane_signs(const uint32_t* signs, int lk, float (&sg)[kEncCpl]) {
@@ -142,6 +152,37 @@ __device__ __forceinline__ uint64_t encode_key_lane(float (&x)[kEncCpl], int lk,
   nrm = rotate_key_lane<D>(x, lk, sg);
   const float inv = unit_scale<D>(nrm);
   return pack_lane_codes<BITS>(x, inv, [&](float y) { return code_by_count<BITS>(y, thresholds); });
+}
+
+// Power-of-two codec (shift-accumulate attention page, English abstract): the lane's 16 elements of one key
+// held on LPK = D/16 lanes (all of them must run this together).  alpha = max_i |k_i| over the whole key;
+// element j gets the index of the magnitude nearest to |k_j| / alpha, counted as the midpoints m with
+// |k_j| < t_m * alpha (a value on a midpoint takes the larger magnitude), and the sign bit k_j < 0 above
+// it.  Returns the lane's 16*BITS packed bits (element 16*lk+j at bits [BITS*j, BITS*j+BITS)).  For fp16
+// keys every comparison is exact in fp32 (alpha has 11 significant bits and a midpoint at most 3).
+template <int D, int BITS>
+__device__ __forceinline__ uint64_t pot_encode_lane(const float (&x)[kEncCpl], const float* thresholds, float& alpha) {
+  constexpr int NM = 1 << (BITS - 1);  // magnitudes
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  alpha = key_lanes_max<EncLanes<D>::LPK>(amax);
+  float lim[NM - 1];
+#pragma unroll
+  for (int m = 0; m < NM - 1; ++m) lim[m] = thresholds[m] * alpha;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) {
+    const float a = fabsf(x[j]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
+    if (x[j] < 0.0f) c |= 1u << (BITS - 1);
+    const int bit = BITS * j;
+    if (bit < 32) lo |= c << bit;
+    if (bit + BITS > 32) hi |= bit >= 32 ? c << (bit - 32) : c >> (32 - bit);
+  }
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Loads the 16 coordinates 16*lk .. 16*lk+15 of the key at `key` (fp16 or fp32, 16-byte aligned rows).

@@ -16,21 +16,11 @@
 
 namespace kvq {
 
-template <int LPK>
-__device__ __forceinline__ float key_lanes_max(float v) {
-  if constexpr (LPK >= 2) v = fmaxf(v, xor_lane<1>(v));
-  if constexpr (LPK >= 4) v = fmaxf(v, xor_lane<2>(v));
-  if constexpr (LPK >= 8) v = fmaxf(v, xor_lane<4>(v));
-  if constexpr (LPK >= 16) v = fmaxf(v, xor_lane<8>(v));
-  return v;
-}
-
 template <int D, int BITS, bool KF16>
 __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
   constexpr int KPB = 256 / LPK;  // keys per workgroup per pass
   constexpr int BPK = D * BITS / 8;
-  constexpr int NM = 1 << (BITS - 1);  // magnitudes
   const int lk = threadIdx.x & (LPK - 1);
   const int64_t n_keys = p.key_end - p.key_begin;
   const int64_t stride = (int64_t)gridDim.x * KPB;
@@ -39,26 +29,8 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   for (int64_t k = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK; k < n_keys; k += stride) {
     float x[kEncCpl];
     load_key_lane<D, KF16>(p.keys, p.key_begin + k, lk, x);
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kEncCpl; ++j) amax = fmaxf(amax, fabsf(x[j]));
-    const float alpha = key_lanes_max<LPK>(amax);
-    float lim[NM - 1];
-#pragma unroll
-    for (int m = 0; m < NM - 1; ++m) lim[m] = p.thresholds[m] * alpha;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < kEncCpl; ++j) {
-      const float a = fabsf(x[j]);
-      uint32_t c = 0;
-#pragma unroll
-      for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
-      if (x[j] < 0.0f) c |= 1u << (BITS - 1);
-      const int bit = BITS * j;
-      if (bit < 32) lo |= c << bit;
-      if (bit + BITS > 32) hi |= bit >= 32 ? c << (bit - 32) : c >> (32 - bit);
-    }
-    const uint64_t packed = ((uint64_t)hi << 32) | lo;
+    float alpha;
+    const uint64_t packed = pot_encode_lane<D, BITS>(x, p.thresholds, alpha);
     const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
     const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
     const uint32_t t = gk - bh * (uint32_t)p.T_new;

@@ -139,3 +139,57 @@ def test_append_graph_replays(K, oracle_mod):
         assert torch.equal(out, eager)
         assert torch.equal(codes, eager_codes)
     assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+
+
+POT_CASES = [
+    # name, shape, batches, T, b, mantissa, seq_lens, n_splits, key dtype
+    ("longctx_b4_ragged", W.LONGCTX, [0, 4, 7], 3000, 4, 0, [3000, 1, 1777], 0, np.float16),
+    ("llama8b_b4_mant", W.LLAMA8B, None, 1500, 4, 1, None, 0, np.float16),
+    ("d32_b3_fp32_len0", W.scaled(W.TINY, d=32, B=2, Hq=2, Hkv=2, T=200), None, None, 3, 1, [0, 200], 3, np.float32),
+    ("d256_b2", W.scaled(W.LONGCTX, d=256, B=2, Hq=4, Hkv=2, T=300), None, None, 2, 0, [300, 129], 0, np.float16),
+]
+
+
+@pytest.mark.parametrize("name,shape,batches,T,b,mant,lens,n_splits,kdt", POT_CASES, ids=[c[0] for c in POT_CASES])
+def test_pot_append_equals_encode_then_attend(K, oracle_mod, name, shape, batches, T, b, mant, lens, n_splits, kdt):
+    """The fused step with power-of-two key codes: bit-identical to encode + decode, and the new keys' codes
+    and scales are the oracle's."""
+    import torch
+    T = shape.T if T is None else T
+    bsel = list(range(shape.B)) if batches is None else list(batches)
+    keys = W.keys(shape, batches=bsel, T=T).astype(kdt)
+    q, v = W.queries(shape)[bsel], W.values(shape, batches=bsel, T=T)
+    newk = W.new_keys(shape)[bsel][:, :, 0, :].astype(kdt)
+    B, Hkv, T_cap, d = keys.shape
+    cb = K.kvq_build_codebook_pot(d, b, mant)
+    ref_c, ref_s, _ = oracle_mod.pot_encode(keys, b, mant)
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    lens_np = np.full(B, T_cap) if lens is None else np.array(lens)
+    log("pot append", name, keys.shape, "b", b, "mantissa", mant, "lens", lens)
+    qd, vd, nk = torch_dev(q), torch_dev(v), torch_dev(newk)
+    codes_a, sc_a = torch_dev(ref_c), torch_dev(ref_s.astype(np.float32))
+    wp = torch.tensor(lens_np - 1, dtype=torch.int32, device="cuda:0")
+    K.kvq_encode_keys(cb, None, nk.unsqueeze(2).contiguous(), codes_a, sc_a, write_pos=wp)
+    out_a = K.kvq_decode_attn(cb, None, qd, codes_a, sc_a, vd, seq_lens=sl, out_dtype=torch.float32, n_splits=n_splits)
+    codes_b, sc_b = torch_dev(ref_c), torch_dev(ref_s.astype(np.float32))
+    out_b = K.kvq_decode_attn_append(cb, None, nk, qd, codes_b, sc_b, vd, seq_lens=sl, out_dtype=torch.float32,
+                                     n_splits=n_splits)
+    torch.cuda.synchronize()
+    assert torch.equal(codes_a, codes_b) and torch.equal(sc_a, sc_b) and torch.equal(out_a, out_b)
+    nc, ns, ntie = oracle_mod.pot_encode(newk[:, :, None, :], b, mant)
+    got_c, got_s = codes_b.cpu().numpy(), sc_b.cpu().numpy()
+    exp_c, exp_s = ref_c.copy(), ref_s.astype(np.float32)
+    for bi in range(B):
+        if lens_np[bi] == 0:
+            continue
+        pos = int(lens_np[bi]) - 1
+        gi = oracle_mod.unpack_codes(got_c[bi, :, pos], d, b)
+        ri = oracle_mod.unpack_codes(nc[bi, :, 0], d, b)
+        assert not np.any((gi != ri) & ~ntie[bi, :, 0])
+        np.testing.assert_array_equal(got_s[bi, :, pos], ns[bi, :, 0].astype(np.float32))
+        exp_c[bi, :, pos] = got_c[bi, :, pos]
+        exp_s[bi, :, pos] = got_s[bi, :, pos]
+    ref = oracle_mod.pot_decode_attn(q, exp_c, exp_s, v, b, mant, scale_of(d), seq_lens=lens)
+    err = rel_l2_rows(out_b.cpu().numpy(), ref)
+    log("  max rel L2 vs oracle %.3g" % float(err.max()))
+    assert np.all(err <= OUT_TOL)
