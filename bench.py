@@ -134,6 +134,32 @@ def cpu_baseline_qv(shape, signs, q, min_seconds=5.0):
                       % (shape.B, shape.Hq, shape.T, passes, elapsed)}
 
 
+def cpu_baseline_pot(shape, q, bits, mantissa, min_seconds=5.0):
+    """Time the fp64 oracle (one thread) on the power-of-two decode step, repeated until min_seconds pass."""
+    import oracle
+    import workloads as W
+
+    scale = 1.0 / math.sqrt(shape.d)
+    cache = []
+    for bi in range(shape.B):  # the prefilled cache, encoded by the oracle itself, untimed
+        codes, scales, _ = oracle.pot_encode(W.keys(shape, batches=[bi]), bits, mantissa)
+        cache.append((codes, scales, W.values(shape, batches=[bi])))
+    newk = W.new_keys(shape)
+    done_keys, elapsed, passes = 0, 0.0, 0
+    while elapsed < min_seconds or passes == 0:
+        t0 = time.perf_counter()
+        oracle.pot_encode(newk, bits, mantissa)                                      # write path of the step
+        for bi, (codes, scales, v) in enumerate(cache):
+            oracle.pot_decode_attn(q[bi:bi + 1], codes, scales, v, bits, mantissa, scale)  # read path
+        elapsed += time.perf_counter() - t0
+        done_keys += shape.B * shape.Hq * shape.T
+        passes += 1
+    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": "the full power-of-two decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode "
+                      "of the new keys + decode attention, one thread, %.1f s"
+                      % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+
+
 def run_suite(K, torch, reps=5, calls=30):
     """Every configuration of the method on one GPU: read path (fused decode, scores alone), write path
     (encode), and the PQ variant.  Inputs are drawn on the GPU from a seeded generator with the workloads'
@@ -371,9 +397,10 @@ def main(argv=None):
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline step, time every workload and operation (table on stderr)")
-    ap.add_argument("--variant", choices=("append", "qv"), default="append",
+    ap.add_argument("--variant", choices=("append", "qv", "pot"), default="append",
                     help="append: the fused append + decode step over fp16 V (default); qv: decode attention "
-                         "with the values stored as codes of the same codec (kvq_decode_attn_qv)")
+                         "with the values stored as codes of the same codec (kvq_decode_attn_qv); pot: the fused "
+                         "step with 4-bit power-of-two key codes (with the mantissa term) instead")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -406,8 +433,11 @@ def main(argv=None):
     v0 = torch.from_numpy(W.values(shape)).to(dev)
     newk = torch.from_numpy(W.new_keys(shape)).to(dev)
     q = torch.from_numpy(q_np).to(dev)
-    cb = K.kvq_build_codebook(d, b)
+    pot = a.variant == "pot"
+    cb = K.kvq_build_codebook_pot(d, b, 1) if pot else K.kvq_build_codebook(d, b)
     bpk = cb.bytes_per_key
+    if pot:
+        signs = None  # no sign pattern: the codec has no rotation
 
     # prefill: encode the whole cache once (setup), then make R copies at distinct addresses
     codes0 = torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev)
@@ -498,7 +528,10 @@ def main(argv=None):
     cpu = None
     if not a.no_cpu_baseline:
         eprint("timing the CPU oracle on a bounded sample (~%.0f s)" % a.cpu_seconds)
-        cpu = (cpu_baseline_qv if qv else cpu_baseline)(shape, signs, q_np, a.cpu_seconds)
+        if pot:
+            cpu = cpu_baseline_pot(shape, q_np, b, 1, a.cpu_seconds)
+        else:
+            cpu = (cpu_baseline_qv if qv else cpu_baseline)(shape, signs, q_np, a.cpu_seconds)
         eprint("cpu oracle: %.4g key-scores/s (%s)" % (cpu["value"], cpu["sample"]))
 
     rec = {
@@ -532,6 +565,14 @@ def main(argv=None):
         rec["roofline"].update({"traffic": measured_traffic(TRAFFIC_FILE_QV),
                                 "kernel": "qv_decode_kernel (MFMA scores from key levels + online softmax + "
                                           "rotated-domain AV from value levels + split merge + inverse transform)"})
+    if pot:
+        rec["config"].update({"workload": "longctx decode, keys as 4-bit power-of-two codes with the mantissa term: "
+                                          "B=8 Hq=32 Hkv=4 d=64 b=4 T=32768, fp16 q/k/v",
+                              "step": "one kvq_decode_attn_append launch with a power-of-two codebook: encode B*Hkv "
+                                      "new keys at T-1 + decode attention over T keys"})
+        rec["roofline"].update({"traffic": None,
+                                "kernel": "decode_kernel<PotScorer> (fused append + shifted-query table score + "
+                                          "online softmax + AV + split merge)"})
     print(json.dumps(rec), flush=True)
     return 0
 
