@@ -143,6 +143,7 @@ kvq_status check_read(const kvq_codebook* cb, const int8_t* signs, const void* q
   if (!q || !codes) return fail(KVQ_ERR_INVALID_ARG, "q or codes is NULL");
   if (!aligned16(q) || !aligned16(codes)) return fail(KVQ_ERR_INVALID_ARG, "q or codes not 16-byte aligned");
   std::memset(p, 0, sizeof *p);
+  p->waves = 8;
   if (cb->kind == KVQ_HADAMARD_LM) {
     if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms is NULL");
     if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
@@ -402,6 +403,9 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
     p.counters = reinterpret_cast<unsigned*>(workspace);
     p.ws = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + counter_bytes);
   }
+  // Workgroups of 12 waves (three per SIMD) pay off only when every wave has several chunks to stream: d = 64,
+  // fp16 V, a scalar codec and splits of at least 4096 tokens; otherwise 8 waves.
+  p.waves = (cb->kind != KVQ_PQ && cb->d == 64 && vdtype == KVQ_F16 && p.split_len >= 4096) ? 12 : 8;
   const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = cb->kind == KVQ_HADAMARD_LM ? kvq::launch_hlm_decode(cb->d, cb->b, rs.gg, vdtype == KVQ_F16, p, grid, s)

@@ -90,7 +90,7 @@ struct ScalarTable {
   // times 2^e_g (fix_exp), so the table of head g sums to at most 2^30 in magnitude along any choice of one
   // entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
   // column); each work item fills JPT consecutive columns of one (head group, row).
-  template <int GG, int HW>
+  template <int GG, int HW, int NT = kThreads>
   __device__ static void build(const AttnParams&, const float* qs, const float* qa, const float* lv, float* lut,
                                int, int tid) {
     using E = typename VecI<HW>::type;
@@ -99,7 +99,7 @@ struct ScalarTable {
     constexpr int total = (GG / HW) * ROWS * NJ;
     const float cmax = level_max(lv);
     E* L = reinterpret_cast<E*>(lut);
-    for (int e = tid; e < total; e += kThreads) {
+    for (int e = tid; e < total; e += NT) {
       const int j0 = (e % NJ) * JPT;
       const int r = (e / NJ) % ROWS;
       const int g0 = (e / (NJ * ROWS)) * HW;
@@ -169,13 +169,13 @@ struct PqScorer {
   }
   __device__ static __forceinline__ float level_max(const float*) { return 1.0f; }
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).
-  template <int GG, int HW>
+  template <int GG, int HW, int NT = kThreads>
   __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
                                int tid) {
     constexpr int total = GG * ROWS * COLS;
     const int K = p.pq_K;
     const float* cent = p.pq_cent + (size_t)kvh * M * K * DS;
-    for (int idx = tid; idx < total; idx += kThreads) {
+    for (int idx = tid; idx < total; idx += NT) {
       const int hh = idx % HW;
       const int c = (idx / HW) % COLS;
       const int s = (idx / (HW * COLS)) % ROWS;
@@ -190,22 +190,22 @@ struct PqScorer {
   }
 };
 
-template <class S, int GG>
+template <class S, int GG, int NWV = kWaves>
 struct LdsPlan {
   static constexpr int HW = GG < 4 ? GG : 4;
   static constexpr int NQ = GG / HW;
   static constexpr size_t lut_bytes = (size_t)GG * S::ROWS * S::COLS * 4;
-  static constexpr size_t red_bytes = (size_t)kWaves * GG * (S::D + 2) * 4;
+  static constexpr size_t red_bytes = (size_t)NWV * GG * (S::D + 2) * 4;
   static constexpr size_t region0 = ((lut_bytes > red_bytes ? lut_bytes : red_bytes) + 15) / 16 * 16;
-  // consts: 16 levels (+0), merge flag (+96), per-wave progress (+128), appended key's codes (+160) and
-  // norm (+288)
+  // consts: 16 levels (+0), merge flag (+96), per-wave progress (+128, up to 16 waves), appended key's codes
+  // (+192) and norm (+320)
   static constexpr size_t consts_off = region0;
-  static constexpr size_t newcode_off = consts_off + 160;
-  static constexpr size_t newnorm_off = consts_off + 288;
-  static constexpr size_t qs_off = consts_off + 304;              // GG * D floats
+  static constexpr size_t newcode_off = consts_off + 192;
+  static constexpr size_t newnorm_off = consts_off + 320;
+  static constexpr size_t qs_off = consts_off + 336;              // GG * D floats
   static constexpr size_t qa_off = qs_off + (size_t)GG * S::D * 4;  // GG floats: sum_i |q'_{g,i}|
   static constexpr size_t pst_off = qa_off + 32;
-  static constexpr size_t pst_bytes(bool f16) { return (size_t)kWaves * GG * kChunk * (f16 ? 2 : 4); }
+  static constexpr size_t pst_bytes(bool f16) { return (size_t)NWV * GG * kChunk * (f16 ? 2 : 4); }
   static constexpr size_t total(bool f16) { return pst_off + pst_bytes(f16); }
 };
 
@@ -236,13 +236,13 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 // `between` runs after this thread's query loads are issued and before they are used: the caller issues
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
-template <class S, int GG, class F>
+template <class S, int GG, int NT = kThreads, class F>
 __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
   if (tid < 16) lv[tid] = p.levels[tid];
   if constexpr (S::kIntLut) {
     constexpr int LPQ = D / 8;  // lanes per query (a power of two <= 32, so groups never straddle waves)
-    static_assert(GG * LPQ <= kThreads, "one lane per 8 coordinates of every query");
+    static_assert(GG * LPQ <= NT, "one lane per 8 coordinates of every query");
     const int g = tid / LPQ, k = tid % LPQ;
     const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + 8 * k;
     const uint32_t sb = (p.signs[(8 * k) >> 5] >> ((8 * k) & 31)) & 0xffu;
@@ -310,7 +310,7 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
     }
   } else {
     between();
-    for (int idx = tid; idx < GG * D; idx += kThreads) {
+    for (int idx = tid; idx < GG * D; idx += NT) {
       const size_t off = ((size_t)u.b * p.Hq + u.h0 + idx / D) * D + idx % D;
       qs[idx] = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off] : reinterpret_cast<const float*>(p.q)[off];
     }
@@ -330,7 +330,7 @@ using ScoreAcc = typename std::conditional<S::kIntLut, uint32_t, float>::type;
 // ahead of the adds that consume them, so 2*4*NQ reads are in flight; the scheduling barriers keep the
 // compiler from folding the stages back together (which would hold every gather of the key in registers).
 // The first stage initialises the sums.
-template <class S, int GG>
+template <class S, int GG, int ST = 4>
 __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut, const uint32_t (&w)[S::NW],
                                            ScoreAcc<S> (&acc)[GG]) {
   constexpr int HW = GG < 4 ? GG : 4;
@@ -339,8 +339,7 @@ __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut
   constexpr int LG = ES == 16 ? 4 : (ES == 8 ? 3 : 2);
   constexpr uint32_t NMASK = 0xFu << LG;
   using E = typename std::conditional<S::kIntLut, typename VecI<HW>::type, typename VecF<HW>::type>::type;
-  constexpr int ST = 4;  // coordinates per stage
-  static_assert(S::ROWS % ST == 0, "rows come in stages of four");
+  static_assert(S::ROWS % ST == 0, "rows come in whole stages");  // ST: rows per stage
   constexpr int NST = S::ROWS / ST;
 
   // byte offset of coordinate i's entry within its row
@@ -515,18 +514,23 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class S, int GG, bool VF16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void decode_kernel(const AttnParams p) {
+// NWV waves per workgroup: 8 (two per SIMD), or 12 (three per SIMD, for d = 64 with fp16 V and long splits:
+// the third wave hides more latency, paid for with a shallower gather pipeline and V requested when its
+// chunk starts rather than one chunk ahead, to fit 168 registers).
+template <class S, int GG, bool VF16, int NWV = 8>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV == 8 ? 1 : NWV / 4, NWV / 4)))
+void decode_kernel(const AttnParams p) {
   constexpr int D = S::D;
   constexpr int DPL = D / 16;  // V columns per lane per MFMA tile set
-  using Plan = LdsPlan<S, GG>;
+  constexpr int NT = 64 * NWV;
+  using Plan = LdsPlan<S, GG, NWV>;
   constexpr int HW = Plan::HW;
   using PT = typename std::conditional<VF16, _Float16, float>::type;
   typedef PT vrow_t __attribute__((ext_vector_type(DPL < 2 ? 2 : DPL)));
   __shared__ __align__(16) unsigned char smem[Plan::total(VF16)];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
   int* s_flag = reinterpret_cast<int*>(smem + Plan::consts_off + 96);
-  volatile int* s_prog = reinterpret_cast<int*>(smem + Plan::consts_off + 128);  // [kWaves] chunks done
+  volatile int* s_prog = reinterpret_cast<int*>(smem + Plan::consts_off + 128);  // [NWV] chunks done
   uint32_t* s_newc = reinterpret_cast<uint32_t*>(smem + Plan::newcode_off);
   float* s_newn = reinterpret_cast<float*>(smem + Plan::newnorm_off);
   static_assert(S::NW * 4 <= 128, "appended key's codes fit their LDS slot");
@@ -562,10 +566,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   // chunk's loads are requested before the prologue so they arrive while the table is built.  Loads past
   // the split's end read as zeros, so the fetches need no guard (a guard would also make the compiler
   // wait for every outstanding load wherever it cannot count them).
-  constexpr int STR = kWaves * kChunk;  // distance between a wave's consecutive chunks
+  constexpr int STR = NWV * kChunk;  // distance between a wave's consecutive chunks
   constexpr int VW = DPL < 2 ? 1 : DPL / 2;  // 32-bit words per fp16 V slice
-  constexpr bool kVPre = VF16 && VW <= 2;
-  constexpr bool kVChunk = VF16 && VW == 4;
+  constexpr bool kVPre = VF16 && VW <= 2 && NWV == 8;
+  constexpr bool kVChunk = VF16 && (VW == 4 || (NWV > 8 && VW <= 4));
   struct Chunk {
     uint32_t w[S::NW];
     float nrm;
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
   // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
   // burst streams in while the queries are rotated and the table is built.
-  prologue<S, GG>(p, u, qs, qa, lv, tid, [&] {
+  prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] {
     fetch_codes(c, ka);
     fetch_v(c, ka);
     const int ko = lane * kEncCpl * kesz;
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     }
   }
-  S::template build<GG, HW>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   if (lane == 0) s_prog[wid] = 0;
   lds_barrier();
   // softmax argument of head g per unit of table sum and of key norm: scale * log2(e) (* 2^-e_g)
@@ -679,7 +683,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
     // ---- scores from the table
     ScoreAcc<S> acc[GG];
-    lut_scores<S, GG>(smem, k.w, acc);
+    lut_scores<S, GG, NWV == 8 ? 4 : 2>(smem, k.w, acc);
     float z[GG];
 #pragma unroll
     for (int g = 0; g < GG; ++g) {
@@ -747,12 +751,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
     wave_lds_sync();
 
-    // ---- keep the two waves that share a SIMD (wid and wid ^ kWaves/2) level: the instruction arbiter
-    // favours the older wave, which would otherwise finish well before its partner and leave the SIMD
-    // half occupied for the rest of the split.  A wave that is ahead drops its priority.
+    // ---- keep the waves that share a SIMD (wid, wid + 4, ...) level: the instruction arbiter favours the
+    // older wave, which would otherwise finish well before its partners and leave the SIMD partly idle for
+    // the rest of the split.  A wave that is ahead of the slowest of its partners drops its priority.
     ++done;
     if (lane == 0) s_prog[wid] = done;
-    const int other = __builtin_amdgcn_readfirstlane(s_prog[wid ^ (kWaves / 2)]);
+    int other = __builtin_amdgcn_readfirstlane(s_prog[(wid + 4) % NWV]);
+#pragma unroll
+    for (int k = 2; k < NWV / 4; ++k) {
+      const int o = __builtin_amdgcn_readfirstlane(s_prog[(wid + 4 * k) % NWV]);
+      other = o < other ? o : other;
+    }
     if (done > other) __builtin_amdgcn_s_setprio(0);
     else __builtin_amdgcn_s_setprio(1);
   };
@@ -771,9 +780,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   for (int g = 0; g < GG; ++g) l_w[g] = wave_sum(l_lane[g]);
   __builtin_amdgcn_s_setprio(0);
   lds_barrier();  // every wave is done with the table, whose space now holds the per-wave partials
-  float* red = reinterpret_cast<float*>(smem);            // [kWaves][GG][D]
-  float* red_m = red + kWaves * GG * D;                    // [kWaves][GG]
-  float* red_l = red_m + kWaves * GG;                      // [kWaves][GG]
+  float* red = reinterpret_cast<float*>(smem);            // [NWV][GG][D]
+  float* red_m = red + NWV * GG * D;                       // [NWV][GG]
+  float* red_l = red_m + NWV * GG;                         // [NWV][GG]
   if (r16 < GG) {
 #pragma unroll
     for (int j = 0; j < DPL; ++j)
@@ -787,15 +796,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       red_l[wid * GG + g] = l_w[g];
     }
   lds_barrier();
-  for (int idx = tid; idx < GG * D; idx += kThreads) {
+  for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, red_m[w2 * GG + g]);
+    for (int w2 = 0; w2 < NWV; ++w2) M = fmaxf(M, red_m[w2 * GG + g]);
     float num = 0.0f, den = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) {
+      for (int w2 = 0; w2 < NWV; ++w2) {
         const float wt = fast_exp2(red_m[w2 * GG + g] - M);
         num += wt * red[(w2 * GG + g) * D + dc];
         den += wt * red_l[w2 * GG + g];
@@ -828,7 +837,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   __syncthreads();
   if (!*s_flag) return;
   const int S_ = p.n_splits;
-  for (int idx = tid; idx < GG * D; idx += kThreads) {
+  for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
     const float* base = p.ws + row * (size_t)S_ * (D + kRecPad);
@@ -938,14 +947,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 
 // The kernels' LDS is static (sized per instantiation), so nothing is requested at launch.
 template <class Kern>
-hipError_t launch_attn(Kern kernel, size_t lds, dim3 grid, hipStream_t s, const AttnParams& p) {
+hipError_t launch_attn(Kern kernel, size_t lds, dim3 grid, hipStream_t s, const AttnParams& p, int threads = kThreads) {
   if (lds > 160 * 1024) return hipErrorNotSupported;
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, p);
   return hipGetLastError();
 }
 
+// p.waves selects the workgroup size: 12 waves are built for d = 64 with fp16 V and the scalar codecs only.
 template <class S, int GG>
 hipError_t run_decode_gg(bool v_f16, const AttnParams& p, dim3 grid, hipStream_t s) {
+  if (p.waves == 12) {
+    if constexpr (S::D == 64 && S::kIntLut) {
+      if (!v_f16) return hipErrorNotSupported;
+      return launch_attn(decode_kernel<S, GG, true, 12>, LdsPlan<S, GG, 12>::total(true), grid, s, p, 12 * 64);
+    }
+    return hipErrorNotSupported;
+  }
   using Plan = LdsPlan<S, GG>;
   if (v_f16) return launch_attn(decode_kernel<S, GG, true>, Plan::total(true), grid, s, p);
   return launch_attn(decode_kernel<S, GG, false>, Plan::total(false), grid, s, p);

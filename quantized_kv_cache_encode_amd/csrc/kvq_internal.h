@@ -45,6 +45,7 @@ struct AttnParams {
   // values as codes of the same codec (kvq_decode_attn_qv): [B][Hkv][T_cap][bytes per key] and norms
   const uint8_t* vcodes;
   const float* vnorms;
+  int waves;                 // decode workgroup size in waves: 8, or 12 (chosen by the host with the splits)
 };
 
 struct EncodeParams {

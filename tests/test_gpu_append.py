@@ -36,6 +36,8 @@ CASES = [
     ("d64_G6_two_groups", W.scaled(W.LONGCTX, B=2, Hq=12, Hkv=2, T=600), None, None, [600, 333], 0, "f16"),
     ("d256_b3", W.scaled(W.LONGCTX, d=256, b=3, B=2, Hq=4, Hkv=2, T=300), None, None, [300, 129], 0, "f16"),
     ("d32_b1_G1", W.scaled(W.TINY, d=32, b=1, B=2, Hq=2, Hkv=2, T=200, dtype="f16"), None, None, None, 0, "f16"),
+    # splits of 4096 tokens: 12-wave workgroups
+    ("longctx_long_splits", W.LONGCTX, [0, 5], 8192, [8192, 6001], 2, "f16"),
 ]
 
 
@@ -102,10 +104,11 @@ def test_append_equals_encode_then_attend(K, oracle_mod, name, shape, batches, T
     np.testing.assert_array_equal(got_codes[untouched], ref_codes[untouched])
 
 
-def test_append_graph_replays(K, oracle_mod):
+@pytest.mark.parametrize("T,n_splits", [(2500, 0), (8192, 2)], ids=["8_waves", "12_waves"])
+def test_append_graph_replays(K, oracle_mod, T, n_splits):
     """The fused step captured in a HIP graph: every replay (with eager work between) equals the eager call."""
     import torch
-    shape = W.scaled(W.LONGCTX, B=2, T=2500)
+    shape = W.scaled(W.LONGCTX, B=2, T=T)
     case = make_hlm_case(shape)
     cb = K.kvq_build_codebook(shape.d, shape.b)
     ref_codes, ref_norms, _ = oracle_cache(oracle_mod, shape, case["keys"], case["signs"])
@@ -113,11 +116,12 @@ def test_append_graph_replays(K, oracle_mod):
     q, v = torch_dev(case["q"]), torch_dev(case["v"])
     nk = torch_dev(W.new_keys(shape)[:, :, 0, :])
     B, Hq, Hkv, T = shape.B, shape.Hq, shape.Hkv, shape.T
-    ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, 0), 16), dtype=torch.uint8, device="cuda:0")
+    ws = torch.zeros(max(K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, n_splits), 16), dtype=torch.uint8,
+                     device="cuda:0")
     out = torch.empty((B, Hq, shape.d), dtype=torch.float16, device="cuda:0")
 
     def step():
-        K.kvq_decode_attn_append(cb, case["signs"], nk, q, codes, norms, v, out=out, workspace=ws)
+        K.kvq_decode_attn_append(cb, case["signs"], nk, q, codes, norms, v, out=out, workspace=ws, n_splits=n_splits)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -147,6 +151,7 @@ POT_CASES = [
     ("llama8b_b4_mant", W.LLAMA8B, None, 1500, 4, 1, None, 0, np.float16),
     ("d32_b3_fp32_len0", W.scaled(W.TINY, d=32, B=2, Hq=2, Hkv=2, T=200), None, None, 3, 1, [0, 200], 3, np.float32),
     ("d256_b2", W.scaled(W.LONGCTX, d=256, B=2, Hq=4, Hkv=2, T=300), None, None, 2, 0, [300, 129], 0, np.float16),
+    ("longctx_long_splits", W.LONGCTX, [3, 4], 8192, 4, 1, [8192, 7000], 2, np.float16),
 ]
 
 

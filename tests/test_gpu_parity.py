@@ -254,6 +254,30 @@ def test_decode_same_result_for_every_split_count(K, oracle_mod):
     assert np.max(rel_l2_rows(outs[-1], ref)) <= OUT_TOL
 
 
+def test_decode_twelve_wave_workgroups(K, oracle_mod):
+    """Splits of 4096 tokens or more at d = 64 with fp16 V run 12-wave workgroups (three waves per SIMD): the
+    same result as 8-wave workgroups (shorter splits) to fp16 rounding of the probabilities, and the oracle's."""
+    import torch
+    shape = W.LONGCTX
+    case = make_hlm_case(shape, batches=[0, 6], T=8192)
+    ref_codes, ref_norms, _ = oracle_cache(oracle_mod, shape, case["keys"], case["signs"])
+    codes, norms = _upload_cache(ref_codes, ref_norms)
+    cb = K.kvq_build_codebook(64, 4)
+    lens = [8192, 6001]
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda:0")
+    outs = {}
+    for ns in (2, 4):  # split_len 4096 (12 waves) and 2048 (8 waves)
+        outs[ns] = K.kvq_decode_attn(cb, case["signs"], torch_dev(case["q"]), codes, norms, torch_dev(case["v"]),
+                                     seq_lens=sl, out_dtype=torch.float32, n_splits=ns).cpu().numpy()
+    assert np.max(rel_l2_rows(outs[2], outs[4])) < 1e-3
+    lv, _ = oracle_mod.codebook(64, 4)
+    ref = oracle_mod.decode_attn(lv, case["signs"], case["q"], ref_codes, ref_norms, case["v"], scale_of(64),
+                                 seq_lens=lens)
+    err = rel_l2_rows(outs[2], ref)
+    log("  12-wave max rel L2 %.3g" % float(err.max()))
+    assert np.all(err <= OUT_TOL)
+
+
 def test_longctx_full_size_sampled(K, oracle_mod):
     """The bench workload at full size (B=8, T=32768) in the bench's launch configuration; sampled batches
     carry the oracle's codes and are compared against the oracle row by row."""
