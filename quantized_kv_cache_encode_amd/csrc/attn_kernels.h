@@ -627,14 +627,16 @@ void decode_kernel(const AttnParams p) {
   });
   if constexpr (S::kIntLut) {
     if (enc_lanes) {
-      float x[kEncCpl];
-#pragma unroll
-      for (int j = 0; j < kEncCpl; ++j)
-        x[j] = p.new_f16 ? h2f((uint16_t)(kraw[j / 2] >> (16 * (j % 2)))) : __builtin_bit_cast(float, kraw[j]);
       float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
       uint64_t packed;
-      if constexpr (S::kRotate) packed = encode_key_lane<D, S::CODE_BITS>(x, lane, p.signs, p.thresholds, nrm);
-      else packed = pot_encode_lane<D, S::CODE_BITS>(x, p.thresholds, nrm);
+      if constexpr (S::kRotate) {
+        packed = encode_key_lane<D, S::CODE_BITS>(kraw, p.new_f16 != 0, lane, p.signs, p.thresholds, nrm);
+      } else {
+        float x[kEncCpl];
+        if (p.new_f16) key_lane_floats<true>(kraw, x);
+        else key_lane_floats<false>(kraw, x);
+        packed = pot_encode_lane<D, S::CODE_BITS>(x, p.thresholds, nrm);
+      }
       store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
       if (lane == 0) *s_newn = nrm;
       if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)

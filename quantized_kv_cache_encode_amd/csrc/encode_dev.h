@@ -66,30 +66,15 @@ __device__ __forceinline__ void lane_signs(const uint32_t* signs, int lk, float 
   for (int j = 0; j < kEncCpl; ++j) sg[j] = ((sb >> j) & 1u) ? -1.0f : 1.0f;
 }
 
-// One key is held by LPK = D/16 consecutive lanes, 16 coordinates per lane: lane lk holds coordinates
-// 16*lk .. 16*lk+15 in x.  All LPK lanes must run this together.  On return x holds those coordinates of
-// H' D k, where H' is the unnormalised Sylvester Walsh-Hadamard matrix, and the result is ||k|| (the same
-// in every lane of the key).  sg are the lane's signs from lane_signs.
-template <int D>
-__device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, const float (&sg)[kEncCpl]) {
+// The butterflies from coordinate distance H0 on: in registers for distances H0 .. 8, then across the key's
+// lanes for distances 16, 32, ... (lane distances 1, 2, ...).  Across lanes the lower lane of a pair keeps
+// x + partner and the upper one partner - x, both as one fused multiply-add with +-1 (the same sums and
+// differences as the in-register stages).
+template <int D, int H0>
+__device__ __forceinline__ void butterflies_from(float (&x)[kEncCpl], int lk) {
   constexpr int LPK = EncLanes<D>::LPK;
-  // explicit fused multiply-adds: the sum is the same wherever this is inlined (a plain x*x + ss would
-  // leave the compiler free to fuse differently in different callers)
-  float ss = x[0] * x[0];
 #pragma unroll
-  for (int j = 1; j < kEncCpl; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
-  ss = key_lanes_sum<LPK>(ss);
-  // signs folded into the first butterflies: (s0 a + s1 c, s0 a - s1 c), each product exact
-#pragma unroll
-  for (int i = 0; i < kEncCpl; i += 2) {
-    const float c = x[i + 1] * sg[i + 1];
-    const float a = x[i];
-    x[i] = __builtin_fmaf(a, sg[i], c);
-    x[i + 1] = __builtin_fmaf(a, sg[i], -c);
-  }
-  // remaining in-register butterflies (coordinate distances 2, 4, 8)
-#pragma unroll
-  for (int h = 2; h < kEncCpl; h <<= 1)
+  for (int h = H0; h < kEncCpl; h <<= 1)
 #pragma unroll
     for (int i = 0; i < kEncCpl; ++i)
       if ((i & h) == 0) {
@@ -97,9 +82,6 @@ __device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, co
         x[i] = a + c;
         x[i + h] = a - c;
       }
-  // cross-lane butterflies (coordinate distances 16, 32, ... = lane distances 1, 2, ...): the lower lane
-  // of a pair keeps x + partner, the upper one partner - x, both as one fused multiply-add with +-1 (the
-  // same sums and differences as the in-register stages)
   auto stage = [&](auto dl_tag) {
     constexpr int DL = decltype(dl_tag)::value;
     const float s = (lk & DL) ? -1.0f : 1.0f;
@@ -110,13 +92,71 @@ __device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, co
   if constexpr (LPK >= 4) stage(std::integral_constant<int, 2>{});
   if constexpr (LPK >= 8) stage(std::integral_constant<int, 4>{});
   if constexpr (LPK >= 16) stage(std::integral_constant<int, 8>{});
-  return __builtin_sqrtf(ss);
 }
 
-// 1 / (||k|| sqrt(d)): scales H' D k to the rotated unit vector y; 0 for a zero key.
+// One key is held by LPK = D/16 consecutive lanes, 16 coordinates per lane: lane lk holds coordinates
+// 16*lk .. 16*lk+15.  All LPK lanes must run the rotation together.  It leaves in x those coordinates of
+// H' D k, where H' is the unnormalised Sylvester Walsh-Hadamard matrix, and returns ||k||^2 (the same in
+// every lane of the key).  x holds the lane's coordinates on entry; sg are the lane's signs from lane_signs.
 template <int D>
-__device__ __forceinline__ float unit_scale(float nrm) {
-  return nrm > 0.0f ? 1.0f / (nrm * __builtin_sqrtf((float)D)) : 0.0f;
+__device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, const float (&sg)[kEncCpl]) {
+  // explicit fused multiply-adds: the sum is the same wherever this is inlined (a plain x*x + ss would
+  // leave the compiler free to fuse differently in different callers)
+  float ss = x[0] * x[0];
+#pragma unroll
+  for (int j = 1; j < kEncCpl; ++j) ss = __builtin_fmaf(x[j], x[j], ss);
+  ss = key_lanes_sum<EncLanes<D>::LPK>(ss);
+  // signs folded into the first butterflies: (s0 a + s1 c, s0 a - s1 c), each product exact
+#pragma unroll
+  for (int i = 0; i < kEncCpl; i += 2) {
+    const float c = x[i + 1] * sg[i + 1];
+    const float a = x[i];
+    x[i] = __builtin_fmaf(a, sg[i], c);
+    x[i + 1] = __builtin_fmaf(a, sg[i], -c);
+  }
+  butterflies_from<D, 2>(x, lk);
+  return ss;
+}
+
+// The packed bits of 16 codes of value 2^(BITS-1), the code of y = 0: what a key whose norm is not finite
+// (an infinite or NaN coordinate, or a sum of squares past the fp32 range) is given.
+template <int BITS>
+__device__ __forceinline__ uint64_t middle_codes() {
+  uint64_t v = 0;
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) v |= (uint64_t)(1u << (BITS - 1)) << (BITS * j);
+  return v;
+}
+
+// The lane's 16 coordinates as floats from their raw bits: packed fp16 halves in raw[0..7] (coordinate 2j
+// in the low half of raw[j]), else fp32.
+template <bool KF16>
+__device__ __forceinline__ void key_lane_floats(const uint32_t (&raw)[kEncCpl], float (&x)[kEncCpl]) {
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j)
+    x[j] = KF16 ? h2f((uint16_t)(raw[j / 2] >> (16 * (j % 2)))) : __builtin_bit_cast(float, raw[j]);
+}
+
+// From ||k||^2: the norm ||k|| (stored with the codes) and the factor 1 / (||k|| sqrt(d)) that scales H' D k
+// to the rotated unit vector y.  Within [2^-100, 2^100] the hardware square root and reciprocal square root
+// (within about one ulp) serve; outside it (a zero, tiny, huge or non-finite sum) the correctly rounded
+// operations.  The factor is 0 for a zero or non-finite norm.
+template <int D>
+__device__ __forceinline__ float unit_scale_ss(float ss, float& nrm) {
+  if (ss >= 0x1p-100f && ss <= 0x1p100f) {
+    nrm = __builtin_amdgcn_sqrtf(ss);
+    return __builtin_amdgcn_rsqf(ss * (float)D);
+  }
+  nrm = __builtin_sqrtf(ss);
+  const float inv = 1.0f / (nrm * __builtin_sqrtf((float)D));
+  return (nrm > 0.0f && inv > 0.0f && inv < INFINITY) ? inv : 0.0f;
+}
+
+// y = x * inv for the lane's coordinates.  For a key with a finite sum of squares every y is then finite with
+// |y| <= 1 up to rounding (0 for a zero key).
+__device__ __forceinline__ void unit_vector(float (&x)[kEncCpl], float inv) {
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) x[j] *= inv;
 }
 
 // code = #{ j : t_j <= y } by comparing with every threshold.
@@ -128,13 +168,13 @@ __device__ __forceinline__ uint32_t code_by_count(float y, const float* threshol
   return c;
 }
 
-// The lane's 16*BITS code bits: coordinate 16*lk+j at bits [BITS*j, BITS*j+BITS), y_j = x_j * inv.
+// The lane's 16*BITS code bits: coordinate 16*lk+j at bits [BITS*j, BITS*j+BITS), from y_j = y[j].
 template <int BITS, class Q>
-__device__ __forceinline__ uint64_t pack_lane_codes(const float (&x)[kEncCpl], float inv, Q&& code_of) {
+__device__ __forceinline__ uint64_t pack_lane_codes(const float (&y)[kEncCpl], Q&& code_of) {
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int j = 0; j < kEncCpl; ++j) {
-    const uint32_t c = code_of(x[j] * inv);
+    const uint32_t c = code_of(y[j]);
     const int bit = BITS * j;
     if (bit < 32) lo |= c << bit;
     if (bit + BITS > 32) hi |= bit >= 32 ? c << (bit - 32) : c >> (32 - bit);
@@ -143,15 +183,21 @@ __device__ __forceinline__ uint64_t pack_lane_codes(const float (&x)[kEncCpl], f
 }
 
 // Encode of one key with the per-threshold comparison (used where a single key is encoded).  Same lane
-// layout and arithmetic as the encode kernel, whose table-driven cell search returns the same count.
+// layout and arithmetic as the encode kernel, whose table-driven cell search returns the same count.  raw
+// holds the lane's 16 coordinates: packed fp16 halves in raw[0..7] (kf16), else fp32 bits.
 template <int D, int BITS>
-__device__ __forceinline__ uint64_t encode_key_lane(float (&x)[kEncCpl], int lk, const uint32_t* signs,
-                                                    const float* thresholds, float& nrm) {
+__device__ __forceinline__ uint64_t encode_key_lane(const uint32_t (&raw)[kEncCpl], bool kf16, int lk,
+                                                    const uint32_t* signs, const float* thresholds, float& nrm) {
+  float x[kEncCpl];
+  if (kf16) key_lane_floats<true>(raw, x);
+  else key_lane_floats<false>(raw, x);
   float sg[kEncCpl];
   lane_signs<D>(signs, lk, sg);
-  nrm = rotate_key_lane<D>(x, lk, sg);
-  const float inv = unit_scale<D>(nrm);
-  return pack_lane_codes<BITS>(x, inv, [&](float y) { return code_by_count<BITS>(y, thresholds); });
+  const float ss = rotate_key_lane<D>(x, lk, sg);
+  const float inv = unit_scale_ss<D>(ss, nrm);
+  if (!(ss <= 0x1.fffffep127f)) return middle_codes<BITS>();
+  unit_vector(x, inv);
+  return pack_lane_codes<BITS>(x, [&](float y) { return code_by_count<BITS>(y, thresholds); });
 }
 
 // Power-of-two codec (shift-accumulate attention page, English abstract): the lane's 16 elements of one key
@@ -185,29 +231,51 @@ __device__ __forceinline__ uint64_t pot_encode_lane(const float (&x)[kEncCpl], c
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Loads the 16 coordinates 16*lk .. 16*lk+15 of the key at `key` (fp16 or fp32, 16-byte aligned rows).
-template <int D, bool KF16>
-__device__ __forceinline__ void load_key_lane(const void* keys, int64_t key, int lk, float (&x)[kEncCpl]) {
-  if constexpr (KF16) {
-    const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(keys) + key * D + lk * kEncCpl);
+// The keys [begin, end) of a launch's key array that one workgroup of 256 lanes encodes, KPB = 256/LPK per
+// pass: the LPK lanes tid/LPK take key begin + pass*KPB + tid/LPK.  Each lane reads its 16 coordinates (32 or
+// 64 contiguous bytes) through a buffer resource over the workgroup's own range, two passes ahead in two
+// register sets, so two fetches stay in flight while a pass computes; a fetch past `end` reads zeros.
+// step(k, raw, refill) gets the key index k and the lane's coordinates as raw bits (packed fp16 halves in
+// raw[0..7], or fp32), and calls refill() once it no longer needs raw (which then starts the fetch two
+// passes ahead into it).  Every lane of a key takes the same trip count, so cross-lane steps see all of
+// them.
+template <int D, bool KF16, class Step>
+__device__ __forceinline__ void walk_keys(const void* keys, int64_t begin, int64_t end, int tid, Step&& step) {
+  constexpr int LPK = EncLanes<D>::LPK;
+  constexpr int KPB = 256 / LPK;
+  constexpr int ESZ = KF16 ? 2 : 4;
+  constexpr int NV = kEncCpl * ESZ / 16;  // 16-byte loads per lane and key
+  const int lk = tid & (LPK - 1);
+  const int n = (int)(end - begin);  // the host keeps n * D * ESZ below 2^31
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(reinterpret_cast<const char*>(keys) + begin * D * ESZ), 0, n * D * ESZ, 0x00020000);
+  auto fetch = [&](int rel, uint32_t (&r)[kEncCpl]) {
+    const int off = rel * D * ESZ + lk * kEncCpl * ESZ;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint4 raw = src[h];
-      const uint32_t r[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int h = 0; h < NV; ++h) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16 * h, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[8 * h + 2 * j] = h2f((uint16_t)(r[j] & 0xffffu));
-        x[8 * h + 2 * j + 1] = h2f((uint16_t)(r[j] >> 16));
-      }
+      for (int j = 0; j < 4; ++j) r[4 * h + j] = v[j];
     }
-  } else {
-    const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(keys) + key * D + lk * kEncCpl);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 a = src[h];
-      x[4 * h] = a.x; x[4 * h + 1] = a.y; x[4 * h + 2] = a.z; x[4 * h + 3] = a.w;
-    }
+  };
+  uint32_t ra[kEncCpl], rb[kEncCpl];
+  int rel = tid / LPK;
+  fetch(rel, ra);
+  fetch(rel + KPB, rb);
+  auto pass = [&](int r, uint32_t (&buf)[kEncCpl]) { step(begin + r, buf, [&] { fetch(r + 2 * KPB, buf); }); };
+  for (; rel < n; rel += 2 * KPB) {
+    pass(rel, ra);
+    if (rel + KPB >= n) break;
+    pass(rel + KPB, rb);
   }
+}
+
+// Keys per workgroup of the encode kernels: contiguous ranges, a multiple of two passes, about 8192
+// workgroups for large launches (a workgroup that streams its own range keeps the mix of key reads and code
+// writes cheaper for the memory than passes strided over the whole array).
+inline int64_t encode_keys_per_block(int64_t n_keys, int kpb) {
+  int64_t per = (n_keys + 8191) / 8192;
+  return (per + 2 * kpb - 1) / (2 * kpb) * (2 * kpb);
 }
 
 // Stores a lane's 16*BITS code bits at its byte offset lk*2*BITS of the key's code row (code rows are

@@ -7,7 +7,8 @@
 // midpoint takes the larger magnitude) and the sign bit k_i < 0 above it; codes are packed LSB-first next
 // to alpha in the norms buffer.  No rotation.
 //
-// Layout: 16 elements per lane, D/16 lanes per key (a wave holds 64/(D/16) keys); alpha is reduced across
+// Layout: 16 elements per lane, D/16 lanes per key (a wave holds 64/(D/16) keys), and each workgroup
+// streams a contiguous range of keys; alpha is reduced across
 // the key's lanes; each lane packs its 16*b bits and stores them at its own byte offset of the key's row.  For
 // fp16 keys every comparison is exact in fp32 (alpha has 11 significant bits and a midpoint at most 3).
 #include "encode_dev.h"
@@ -19,16 +20,17 @@ namespace kvq {
 template <int D, int BITS, bool KF16>
 __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
-  constexpr int KPB = 256 / LPK;  // keys per workgroup per pass
   constexpr int BPK = D * BITS / 8;
   const int lk = threadIdx.x & (LPK - 1);
   const int64_t n_keys = p.key_end - p.key_begin;
-  const int64_t stride = (int64_t)gridDim.x * KPB;
   auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t { return (__umulhi(n, magic) + n) >> shift; };
-  // every lane of a key takes the same trip count, so the cross-lane reduction sees all of them
-  for (int64_t k = (int64_t)blockIdx.x * KPB + threadIdx.x / LPK; k < n_keys; k += stride) {
+  const int64_t kb = (int64_t)blockIdx.x * p.keys_per_block;
+  const int64_t ke = kb + p.keys_per_block < n_keys ? kb + p.keys_per_block : n_keys;
+  const void* keys = reinterpret_cast<const char*>(p.keys) + p.key_begin * D * (KF16 ? 2 : 4);
+  walk_keys<D, KF16>(keys, kb, ke, threadIdx.x, [&](int64_t k, uint32_t (&raw)[kEncCpl], auto&& refill) {
     float x[kEncCpl];
-    load_key_lane<D, KF16>(p.keys, p.key_begin + k, lk, x);
+    key_lane_floats<KF16>(raw, x);
+    refill();
     float alpha;
     const uint64_t packed = pot_encode_lane<D, BITS>(x, p.thresholds, alpha);
     const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
@@ -37,24 +39,32 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
     int64_t pos = (int64_t)t;
     if (p.write_pos) pos += p.write_pos[fdiv(bh, p.hkv_magic, p.hkv_shift)];
     else pos += p.t0;
-    if (pos < 0 || pos >= p.T_cap) continue;
+    if (pos < 0 || pos >= p.T_cap) return;
     const int64_t row = (int64_t)bh * p.T_cap + pos;
     store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = alpha;
-  }
+  });
 }
 
 template <int D, int BITS>
 static hipError_t pot_launch(bool kf16, const EncodeParams& p0, hipStream_t s) {
   constexpr int KPB = 256 / EncLanes<D>::LPK;
-  EncodeParams p = p0;
-  p.key_begin = 0;
-  p.key_end = (int64_t)p0.B * p0.Hkv * p0.T_new;
-  const int64_t blocks = (p.key_end + KPB - 1) / KPB;
-  const dim3 grid((unsigned)(blocks < 2048 ? blocks : 2048));
-  if (kf16) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  const int64_t n_keys = (int64_t)p0.B * p0.Hkv * p0.T_new;
+  // launches of at most 2^30 key bytes each (key indices stay below 2^31); each workgroup encodes a
+  // contiguous range of keys
+  const int64_t per_launch = ((int64_t)1 << 30) / (D * (kf16 ? 2 : 4));
+  for (int64_t k0 = 0; k0 < n_keys; k0 += per_launch) {
+    EncodeParams p = p0;
+    p.key_begin = k0;
+    p.key_end = k0 + per_launch < n_keys ? k0 + per_launch : n_keys;
+    p.keys_per_block = encode_keys_per_block(p.key_end - p.key_begin, KPB);
+    const dim3 grid((unsigned)((p.key_end - p.key_begin + p.keys_per_block - 1) / p.keys_per_block));
+    if (kf16) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false>), grid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int D>
