@@ -266,9 +266,13 @@ def run_suite(K, torch, reps=5, calls=30):
         row(name, "append+dec", timed(app, n_rot), algorithmic_bytes(sh, bpk, append=True), B * Hq * T, B * Hkv * T)
         row(name, "score", timed(score, n_rot), B * Hkv * T * (bpk + 4) + B * Hq * T * 4, B * Hq * T, B * Hkv * T)
 
+        # the encode reads its keys from n_rot copies too, so that they stream from HBM rather than the
+        # last-level cache
+        key_srcs = [keys] + [keys.clone() for _ in range(n_rot - 1)]
+
         def enc(i):
             c, n, _ = caches[i % n_rot]
-            K.kvq_encode_keys(cb, signs, keys, c, n)
+            K.kvq_encode_keys(cb, signs, key_srcs[i % n_rot], c, n)
 
         row(name, "encode", timed(enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
 
@@ -311,13 +315,13 @@ def run_suite(K, torch, reps=5, calls=30):
 
             def pot_enc(i):
                 c, n = pcs[i % n_rot]
-                K.kvq_encode_keys(pcb, None, keys, c, n)
+                K.kvq_encode_keys(pcb, None, key_srcs[i % n_rot], c, n)
 
             tag = "pot-m" if mant else "pot"
             row(name, tag + "-decode", timed(pot_dec, n_rot), rd, B * Hq * T, B * Hkv * T)
             row(name, tag + "-encode", timed(pot_enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
             del pcs
-        del caches, keys, scores
+        del caches, keys, key_srcs, scores
         torch.cuda.empty_cache()
 
     # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes: byte codes (K = 256) and
