@@ -292,6 +292,7 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
   p.t0 = t0;
   p.B = B;
   p.Hkv = Hkv;
+  p.rows_whole = !write_pos && t0 == 0 && T_new == T_cap;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cb->kind == KVQ_HADAMARD_LM) {
     if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms is NULL");

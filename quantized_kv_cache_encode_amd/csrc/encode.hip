@@ -53,9 +53,6 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
     const float2 e = cells[c];
     return (uint32_t)__builtin_bit_cast(int, e.y) + (y >= e.x ? 1u : 0u);
   };
-  auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t {
-    return (__umulhi(n, magic) + n) >> shift;
-  };
   const int64_t n_keys = p.key_end - p.key_begin;
   const int64_t kb = (int64_t)blockIdx.x * p.keys_per_block;
   const int64_t ke = kb + p.keys_per_block < n_keys ? kb + p.keys_per_block : n_keys;
@@ -73,14 +70,8 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
       packed = pack_lane_codes<BITS>(x, code_of);
     }
 
-    const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
-    const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
-    const uint32_t t = gk - bh * (uint32_t)p.T_new;
-    int64_t pos = (int64_t)t;
-    if (p.write_pos) pos += p.write_pos[fdiv(bh, p.hkv_magic, p.hkv_shift)];
-    else pos += p.t0;
-    if (pos < 0 || pos >= p.T_cap) return;
-    const int64_t row = (int64_t)bh * p.T_cap + pos;
+    const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
+    if (row < 0) return;
     store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = nrm;
   });

@@ -270,12 +270,28 @@ __device__ __forceinline__ void walk_keys(const void* keys, int64_t begin, int64
   }
 }
 
-// Keys per workgroup of the encode kernels: contiguous ranges, a multiple of two passes, about 8192
-// workgroups for large launches (a workgroup that streams its own range keeps the mix of key reads and code
-// writes cheaper for the memory than passes strided over the whole array).
+// The cache row of key gk (an index into [B*Hkv*T_new], below 2^31) of an encode launch with parameters p,
+// or -1 where its position falls outside [0, T_cap): row = (b*Hkv + h)*T_cap + pos, with pos = t +
+// write_pos[b] or t + t0.  Where the new keys fill whole rows the row is gk itself.
+template <class P>
+__device__ __forceinline__ int64_t encode_row(const P& p, uint32_t gk) {
+  if (p.rows_whole) return gk;
+  auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t { return (__umulhi(n, magic) + n) >> shift; };
+  const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
+  const uint32_t t = gk - bh * (uint32_t)p.T_new;
+  int64_t pos = (int64_t)t;
+  if (p.write_pos) pos += p.write_pos[fdiv(bh, p.hkv_magic, p.hkv_shift)];
+  else pos += p.t0;
+  if (pos < 0 || pos >= p.T_cap) return -1;
+  return (int64_t)bh * p.T_cap + pos;
+}
+
+// Keys per workgroup of the encode kernels: contiguous ranges, whole passes, about 8192 workgroups for large
+// launches (a workgroup that streams its own range keeps the mix of key reads and code writes cheaper for the
+// memory than passes strided over the whole array) and one pass each for small ones.
 inline int64_t encode_keys_per_block(int64_t n_keys, int kpb) {
-  int64_t per = (n_keys + 8191) / 8192;
-  return (per + 2 * kpb - 1) / (2 * kpb) * (2 * kpb);
+  const int64_t per = (n_keys + 8191) / 8192;
+  return (per + kpb - 1) / kpb * kpb;
 }
 
 // Stores a lane's 16*BITS code bits at its byte offset lk*2*BITS of the key's code row (code rows are

@@ -66,6 +66,7 @@ struct EncodeParams {
   float cell_inv, cell_shift;
   int64_t key_begin, key_end;  // the keys [key_begin, key_end) of [B*Hkv*T_new] this launch encodes
   int64_t keys_per_block;      // the contiguous keys each workgroup encodes (Hadamard and power-of-two)
+  int rows_whole;              // T_new == T_cap, t0 == 0 and no write_pos: key i of the launch goes to row i
   uint32_t tnew_magic, hkv_magic;  // n / T_new and n / Hkv for n < 2^31: (umulhi(n, magic) + n) >> shift
   int tnew_shift, hkv_shift;
 };

@@ -23,7 +23,6 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   constexpr int BPK = D * BITS / 8;
   const int lk = threadIdx.x & (LPK - 1);
   const int64_t n_keys = p.key_end - p.key_begin;
-  auto fdiv = [](uint32_t n, uint32_t magic, int shift) -> uint32_t { return (__umulhi(n, magic) + n) >> shift; };
   const int64_t kb = (int64_t)blockIdx.x * p.keys_per_block;
   const int64_t ke = kb + p.keys_per_block < n_keys ? kb + p.keys_per_block : n_keys;
   const void* keys = reinterpret_cast<const char*>(p.keys) + p.key_begin * D * (KF16 ? 2 : 4);
@@ -33,14 +32,8 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
     refill();
     float alpha;
     const uint64_t packed = pot_encode_lane<D, BITS>(x, p.thresholds, alpha);
-    const uint32_t gk = (uint32_t)(p.key_begin + k);  // key index in [B*Hkv*T_new] (< 2^31)
-    const uint32_t bh = fdiv(gk, p.tnew_magic, p.tnew_shift);
-    const uint32_t t = gk - bh * (uint32_t)p.T_new;
-    int64_t pos = (int64_t)t;
-    if (p.write_pos) pos += p.write_pos[fdiv(bh, p.hkv_magic, p.hkv_shift)];
-    else pos += p.t0;
-    if (pos < 0 || pos >= p.T_cap) return;
-    const int64_t row = (int64_t)bh * p.T_cap + pos;
+    const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
+    if (row < 0) return;
     store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = alpha;
   });
