@@ -40,6 +40,22 @@ kvq_status from_hip(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// The power-of-two codebook for (d, b, mantissa), arguments already checked: magnitudes 2^-j (or, with the
+// mantissa term, 2^-(j/2) and (3/4) 2^-((j-1)/2) alternately), the signed level of every code value (sign in
+// the top bit) and the midpoints of consecutive magnitudes.
+void pot_codebook(int d, int b, int mantissa, kvq_codebook* out) {
+  std::memset(out, 0, sizeof *out);
+  const int nm = 1 << (b - 1);
+  double mag[8];
+  for (int j = 0; j < nm; ++j) mag[j] = mantissa ? std::ldexp(j % 2 ? 0.75 : 1.0, -(j / 2)) : std::ldexp(1.0, -j);
+  for (int c = 0; c < 2 * nm; ++c) out->levels[c] = (float)(c >= nm ? -mag[c - nm] : mag[c]);
+  for (int j = 0; j + 1 < nm; ++j) out->thresholds[j] = (float)(0.5 * (mag[j] + mag[j + 1]));
+  out->kind = KVQ_POT;
+  out->d = d;
+  out->b = b;
+  out->m = mantissa;
+}
+
 kvq_status check_codebook(const kvq_codebook* cb) {
   if (!cb) return fail(KVQ_ERR_INVALID_ARG, "codebook is NULL");
   if (cb->kind == KVQ_HADAMARD_LM) {
@@ -53,6 +69,15 @@ kvq_status check_codebook(const kvq_codebook* cb) {
       return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", cb->d);
     if (cb->b < 2 || cb->b > 4) return fail(KVQ_ERR_INVALID_ARG, "power-of-two b=%d: must be 2..4", cb->b);
     if (cb->m != 0 && cb->m != 1) return fail(KVQ_ERR_INVALID_ARG, "power-of-two mantissa flag %d: must be 0 or 1", cb->m);
+    // the kernels rely on the canonical levels and midpoints (powers of two, and 3/4 of them with the
+    // mantissa term); anything else is rejected
+    kvq_codebook ref;
+    pot_codebook(cb->d, cb->b, cb->m, &ref);
+    for (int c = 0; c < (2 << (cb->b - 1)); ++c)
+      if (cb->levels[c] != ref.levels[c]) return fail(KVQ_ERR_INVALID_ARG, "power-of-two level %d is not canonical", c);
+    for (int j = 0; j + 1 < (1 << (cb->b - 1)); ++j)
+      if (cb->thresholds[j] != ref.thresholds[j])
+        return fail(KVQ_ERR_INVALID_ARG, "power-of-two midpoint %d is not canonical", j);
     return KVQ_OK;
   }
   if (cb->kind == KVQ_PQ) {
@@ -216,17 +241,7 @@ kvq_status kvq_build_codebook_pot(int d, int b, int mantissa, kvq_codebook* out)
   if (!pow2(d) || d < 16 || d > 256) return fail(KVQ_ERR_INVALID_ARG, "d=%d: must be a power of two in [16, 256]", d);
   if (b < 2 || b > 4) return fail(KVQ_ERR_INVALID_ARG, "b=%d: must be 2..4", b);
   if (mantissa != 0 && mantissa != 1) return fail(KVQ_ERR_INVALID_ARG, "mantissa=%d: must be 0 or 1", mantissa);
-  std::memset(out, 0, sizeof *out);
-  const int nm = 1 << (b - 1);
-  double mag[8];
-  for (int j = 0; j < nm; ++j)  // 2^-j, or with the mantissa term 2^-(j/2) and (3/4) 2^-((j-1)/2) alternately
-    mag[j] = mantissa ? std::ldexp(j % 2 ? 0.75 : 1.0, -(j / 2)) : std::ldexp(1.0, -j);
-  for (int c = 0; c < 2 * nm; ++c) out->levels[c] = (float)(c >= nm ? -mag[c - nm] : mag[c]);
-  for (int j = 0; j + 1 < nm; ++j) out->thresholds[j] = (float)(0.5 * (mag[j] + mag[j + 1]));
-  out->kind = KVQ_POT;
-  out->d = d;
-  out->b = b;
-  out->m = mantissa;
+  pot_codebook(d, b, mantissa, out);
   return ok();
 }
 
@@ -313,6 +328,7 @@ kvq_status kvq_encode_keys(const kvq_codebook* cb, const int8_t* signs, const vo
     if (!norms) return fail(KVQ_ERR_INVALID_ARG, "norms (per-key scales) is NULL");
     if (!aligned16(norms)) return fail(KVQ_ERR_INVALID_ARG, "norms not 16-byte aligned");
     for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << (cb->b - 1)) ? cb->thresholds[j] : 0.0f;
+    p.pot_mant = cb->m;
     if (T_new > 0 && (int64_t)B * Hkv * T_new >= ((int64_t)1 << 31))
       return fail(KVQ_ERR_UNSUPPORTED, "B*Hkv*T_new must stay below 2^31");
     if (T_new > 0) kvq::fast_div_magic((uint32_t)T_new, &p.tnew_magic, &p.tnew_shift);
@@ -384,10 +400,12 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
     p.new_f16 = kdtype == KVQ_F16;
     p.app_codes = const_cast<uint8_t*>(codes);
     p.app_norms = const_cast<float*>(norms);
-    if (cb->kind == KVQ_POT)  // midpoints of the 2^(b-1) magnitudes
+    if (cb->kind == KVQ_POT) {  // midpoints of the 2^(b-1) magnitudes
       for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << (cb->b - 1)) ? cb->thresholds[j] : 0.0f;
-    else
+      p.pot_mant = cb->m;
+    } else {
       for (int j = 0; j < 15; ++j) p.thresholds[j] = j + 1 < (1 << cb->b) ? cb->thresholds[j] : INFINITY;
+    }
   }
   p.seq_lens = seq_lens;
   p.v = v;

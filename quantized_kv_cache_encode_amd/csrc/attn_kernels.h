@@ -635,7 +635,8 @@ void decode_kernel(const AttnParams p) {
         float x[kEncCpl];
         if (p.new_f16) key_lane_floats<true>(kraw, x);
         else key_lane_floats<false>(kraw, x);
-        packed = pot_encode_lane<D, S::CODE_BITS>(x, p.thresholds, nrm);
+        packed = p.pot_mant ? pot_encode_lane<D, S::CODE_BITS, true>(x, p.thresholds, nrm)
+                           : pot_encode_lane<D, S::CODE_BITS, false>(x, p.thresholds, nrm);
       }
       store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
       if (lane == 0) *s_newn = nrm;

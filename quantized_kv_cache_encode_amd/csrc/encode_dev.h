@@ -200,33 +200,61 @@ __device__ __forceinline__ uint64_t encode_key_lane(const uint32_t (&raw)[kEncCp
   return pack_lane_codes<BITS>(x, [&](float y) { return code_by_count<BITS>(y, thresholds); });
 }
 
+__device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
 // Power-of-two codec (shift-accumulate attention page, English abstract): the lane's 16 elements of one key
 // held on LPK = D/16 lanes (all of them must run this together).  alpha = max_i |k_i| over the whole key;
 // element j gets the index of the magnitude nearest to |k_j| / alpha, counted as the midpoints m with
 // |k_j| < t_m * alpha (a value on a midpoint takes the larger magnitude), and the sign bit k_j < 0 above
 // it.  Returns the lane's 16*BITS packed bits (element 16*lk+j at bits [BITS*j, BITS*j+BITS)).  For fp16
 // keys every comparison is exact in fp32 (alpha has 11 significant bits and a midpoint at most 3).
-template <int D, int BITS>
+//
+// The midpoints are canonical (the host checks): t_m = (3/4) 2^-m, or with the mantissa term (MANT)
+// (7/8) 2^-i for m = 2i and (5/8) 2^-i for m = 2i+1.  So the limits are L 2^-k for L = fl(tau * alpha),
+// tau = t_0 or t_1; for alpha in [2^-100, 2^100] every L 2^-k used is a normal float whose bit pattern is
+// bits(L) - k 2^23, and a non-negative float (a NaN counting as above everything, as in a comparison) lies
+// below a positive normal one exactly when its bit pattern does.  Hence #{k < K : a < L 2^-k} =
+// clamp(ceil((bits(L) - bits(a)) / 2^23), 0, K): one subtraction, shift and clamp per family instead of
+// one comparison per midpoint.  Other scales take the comparisons.
+template <int D, int BITS, bool MANT>
 __device__ __forceinline__ uint64_t pot_encode_lane(const float (&x)[kEncCpl], const float* thresholds, float& alpha) {
   constexpr int NM = 1 << (BITS - 1);  // magnitudes
   float amax = 0.0f;
 #pragma unroll
   for (int j = 0; j < kEncCpl; ++j) amax = fmaxf(amax, fabsf(x[j]));
   alpha = key_lanes_max<EncLanes<D>::LPK>(amax);
-  float lim[NM - 1];
-#pragma unroll
-  for (int m = 0; m < NM - 1; ++m) lim[m] = thresholds[m] * alpha;
   uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int j = 0; j < kEncCpl; ++j) {
-    const float a = fabsf(x[j]);
-    uint32_t c = 0;
-#pragma unroll
-    for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
-    if (x[j] < 0.0f) c |= 1u << (BITS - 1);
+  auto put = [&](int j, uint32_t c) {
     const int bit = BITS * j;
     if (bit < 32) lo |= c << bit;
     if (bit + BITS > 32) hi |= bit >= 32 ? c << (bit - 32) : c >> (32 - bit);
+  };
+  if (alpha >= 0x1p-100f && alpha <= 0x1p100f) {
+    constexpr int k1 = MANT ? NM / 2 : NM - 1;  // midpoints of the first family (t_0 2^-k), and of the second
+    constexpr int k2 = MANT ? NM / 2 - 1 : 0;
+    const int r1 = __builtin_bit_cast(int, thresholds[0] * alpha) + 0x7fffff;
+    const int r2 = k2 > 0 ? __builtin_bit_cast(int, thresholds[k2 > 0 ? 1 : 0] * alpha) + 0x7fffff : 0;
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) {
+      const int ba = __builtin_bit_cast(int, fabsf(x[j]));
+      uint32_t c = (uint32_t)clamp_int((r1 - ba) >> 23, 0, k1);
+      if constexpr (k2 > 0) c += (uint32_t)clamp_int((r2 - ba) >> 23, 0, k2);
+      if (x[j] < 0.0f) c |= 1u << (BITS - 1);
+      put(j, c);
+    }
+  } else {
+    float lim[NM - 1];
+#pragma unroll
+    for (int m = 0; m < NM - 1; ++m) lim[m] = thresholds[m] * alpha;
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) {
+      const float a = fabsf(x[j]);
+      uint32_t c = 0;
+#pragma unroll
+      for (int m = 0; m < NM - 1; ++m) c += a < lim[m] ? 1u : 0u;
+      if (x[j] < 0.0f) c |= 1u << (BITS - 1);
+      put(j, c);
+    }
   }
   return ((uint64_t)hi << 32) | lo;
 }

@@ -41,6 +41,7 @@ struct AttnParams {
   uint8_t* app_codes;        // the code cache, written at the new rows (same buffer as codes)
   float* app_norms;          // the norm cache, written at the new rows (same buffer as norms)
   int new_f16;
+  int pot_mant;              // power-of-two codec: the mantissa term is on (fused append)
   float thresholds[15];
   // values as codes of the same codec (kvq_decode_attn_qv): [B][Hkv][T_cap][bytes per key] and norms
   const uint8_t* vcodes;
@@ -67,6 +68,7 @@ struct EncodeParams {
   int64_t key_begin, key_end;  // the keys [key_begin, key_end) of [B*Hkv*T_new] this launch encodes
   int64_t keys_per_block;      // the contiguous keys each workgroup encodes (Hadamard and power-of-two)
   int rows_whole;              // T_new == T_cap, t0 == 0 and no write_pos: key i of the launch goes to row i
+  int pot_mant;                // power-of-two codec: the mantissa term is on
   uint32_t tnew_magic, hkv_magic;  // n / T_new and n / Hkv for n < 2^31: (umulhi(n, magic) + n) >> shift
   int tnew_shift, hkv_shift;
 };

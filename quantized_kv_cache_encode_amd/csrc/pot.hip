@@ -17,7 +17,7 @@
 
 namespace kvq {
 
-template <int D, int BITS, bool KF16>
+template <int D, int BITS, bool KF16, bool MANT>
 __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
   constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
   constexpr int BPK = D * BITS / 8;
@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
     key_lane_floats<KF16>(raw, x);
     refill();
     float alpha;
-    const uint64_t packed = pot_encode_lane<D, BITS>(x, p.thresholds, alpha);
+    const uint64_t packed = pot_encode_lane<D, BITS, MANT>(x, p.thresholds, alpha);
     const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
     if (row < 0) return;
     store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
@@ -52,8 +52,10 @@ static hipError_t pot_launch(bool kf16, const EncodeParams& p0, hipStream_t s) {
     p.key_end = k0 + per_launch < n_keys ? k0 + per_launch : n_keys;
     p.keys_per_block = encode_keys_per_block(p.key_end - p.key_begin, KPB);
     const dim3 grid((unsigned)((p.key_end - p.key_begin + p.keys_per_block - 1) / p.keys_per_block));
-    if (kf16) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false>), grid, dim3(256), 0, s, p);
+    if (kf16 && p.pot_mant) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true, true>), grid, dim3(256), 0, s, p);
+    else if (kf16) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, true, false>), grid, dim3(256), 0, s, p);
+    else if (p.pot_mant) hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((pot_encode_kernel<D, BITS, false, false>), grid, dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -114,6 +114,43 @@ def test_pot_encode_per_batch_write_positions(K, oracle_mod):
         assert not got_c[b][:, untouched].any() and not got_s[b][:, untouched].any()
 
 
+def _midpoint_keys(oracle_mod, b, mant, d, alphas, dtype):
+    """Keys whose elements sit exactly on every midpoint times alpha, one ulp (of dtype) either side of it,
+    on 0 and -0, with both signs; element 0 of each key is +-alpha itself."""
+    mags, thr = oracle_mod.pot_levels(b, mant)
+    rows = []
+    for alpha in alphas:
+        vals = []
+        for t in thr:
+            m = dtype(t * alpha)
+            vals += [m, np.nextafter(m, dtype(np.inf)), np.nextafter(m, dtype(0))]
+        vals += [dtype(0.0), dtype(-0.0), dtype(alpha * 0.5 ** (len(mags) + 2))]
+        vals = np.array(vals, dtype=dtype)
+        for sign in (1, -1):
+            row = np.zeros(d, dtype=dtype)
+            row[0] = dtype(sign * alpha)
+            body = np.resize(np.concatenate([vals, -vals]), d - 1)
+            row[1:] = body
+            rows.append(row)
+    return np.stack(rows)[None, None]  # [1][1][rows][d]
+
+
+@pytest.mark.parametrize("b,mant", [(2, 0), (2, 1), (3, 0), (3, 1), (4, 0), (4, 1)])
+def test_pot_encode_on_midpoints(K, oracle_mod, b, mant):
+    """Elements exactly on the midpoints (times alpha) and one ulp either side: every decision is exact on
+    both sides, so the codes match the oracle bit for bit, for fp16 keys and for fp32 keys at ordinary,
+    tiny (below 2^-100) and huge (above 2^100) scales, which take the comparison path."""
+    d = 64
+    cb = K.kvq_build_codebook_pot(d, b, mant)
+    for dtype, alphas in ((np.float16, [1.0, 3.0 * 2.0 ** -5, 1.5 * 2.0 ** 7]),
+                          (np.float32, [1.0, 1.25 * 2.0 ** -40, 2.0 ** -110, 1.75 * 2.0 ** 110])):
+        keys = _midpoint_keys(oracle_mod, b, mant, d, alphas, dtype)
+        got_c, got_s = _gpu_encode(K, cb, keys)
+        ref_c, ref_s, _ = oracle_mod.pot_encode(keys, b, mant)
+        np.testing.assert_array_equal(got_s, ref_s.astype(np.float32))
+        np.testing.assert_array_equal(got_c, ref_c)
+
+
 def _upload(ref_c, ref_s):
     return torch_dev(ref_c), torch_dev(ref_s.astype(np.float32))
 
