@@ -276,6 +276,12 @@ def test_pot_validation(K):
     bad = K.kvq_build_codebook_pot(64, 4, 1)
     bad.m = 3
     assert _call_encode(K, bad, None) == K.KVQ_ERR_INVALID_ARG
+    # the kernels rely on the canonical levels and midpoints: anything else is rejected
+    for field, idx in (("thresholds", 2), ("levels", 9)):
+        odd = K.kvq_build_codebook_pot(64, 4, 0)
+        getattr(odd, field)[idx] *= 1.01
+        assert _call_encode(K, odd, None) == K.KVQ_ERR_INVALID_ARG
+        assert "canonical" in K.kvq_last_error()
     P = ctypes.c_void_p
     lib = K._lib
     assert lib.kvq_score(ctypes.byref(cb), None, P(FAKE), 1, P(FAKE), None, 1, 4, 2, 128, None, P(FAKE),
