@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # the digest recorded with the counters; after any change to them the figure is stale and traffic is null.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_longctx_hbm_traffic.txt")
 TRAFFIC_FILE_QV = os.path.join(ROOT, "profiles", "qv_decode_kernel_longctx_hbm_traffic.txt")
+TRAFFIC_FILE_ENC = os.path.join(ROOT, "profiles", "hlm_encode_kernel_sweep_b4_B64_hbm_traffic.txt")
 
 
 def library_source_digest():
@@ -158,6 +159,108 @@ def cpu_baseline_pot(shape, q, bits, mantissa, min_seconds=5.0):
             "sample": "the full power-of-two decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode "
                       "of the new keys + decode attention, one thread, %.1f s"
                       % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+
+
+def cpu_baseline_encode(shape, signs, min_seconds=5.0):
+    """Time the fp64 oracle's encode (one thread) on batch 0 of the workload, repeated until min_seconds pass."""
+    import oracle
+    import workloads as W
+
+    _, th = oracle.codebook(shape.d, shape.b)
+    keys = W.keys(shape, batches=[0])
+    done, elapsed, passes = 0, 0.0, 0
+    while elapsed < min_seconds or passes == 0:
+        t0 = time.perf_counter()
+        oracle.encode_keys(th, signs, keys, shape.b)
+        elapsed += time.perf_counter() - t0
+        done += keys.shape[0] * keys.shape[1] * keys.shape[2]
+        passes += 1
+    return {"value": done / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
+            "sample": "batch 0 of the workload (Hkv=%d x T=%d keys, d=%d) x %d pass(es): fp64 C oracle encode, one "
+                      "thread, %.1f s" % (shape.Hkv, shape.T, shape.d, passes, elapsed)}
+
+
+def run_encode(K, torch, a):
+    """The write path at the batch-64 sweep shape (B=64, Hkv=8, T=8192, d=128, b=4, fp16 keys with
+    per-(kv head, channel) LogNormal(0,1) scales): kvq_encode_keys over the whole cache, replayed from a HIP
+    graph, with two key sources and four code/norm buffers in rotation."""
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    shape = next(s for s in W.SWEEP if s.b == 4 and s.B == 64)
+    B, Hkv, d, T, b = shape.B, shape.Hkv, shape.d, shape.T, shape.b
+    eprint("generating %s: B=%d Hkv=%d d=%d b=%d T=%d" % (shape.name, B, Hkv, d, b, T))
+    signs = W.signs(shape)
+    cb = K.kvq_build_codebook(d, b)
+    bpk = cb.bytes_per_key
+    keys0 = torch.empty((B, Hkv, T, d), dtype=torch.float16, device=dev)
+    for bi in range(B):  # the workload's seeded keys, one batch at a time
+        keys0[bi] = torch.from_numpy(W.keys(shape, batches=[bi])[0]).to(dev)
+    srcs = [keys0, keys0.clone()]
+    outs = [(torch.empty((B, Hkv, T, bpk), dtype=torch.uint8, device=dev),
+             torch.empty((B, Hkv, T), dtype=torch.float32, device=dev)) for _ in range(4)]
+
+    def step(i):
+        c, n = outs[i % len(outs)]
+        K.kvq_encode_keys(cb, signs, srcs[i % len(srcs)], c, n)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(a.warmup, len(outs))):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(a.steps):
+            step(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    g.replay()
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / a.steps
+    if a.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    n_keys = B * Hkv * T
+    value = n_keys / (ms_per_step * 1e-3)
+    alg_bytes = n_keys * (2 * d + bpk + 4)
+    achieved = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    eprint("encode %.4f ms -> %.4g keys/s; %d algorithmic bytes -> %.1f GB/s = %.1f%% of %.0f GB/s" %
+           (ms_per_step, value, alg_bytes, achieved, 100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    cpu = None
+    if not a.no_cpu_baseline:
+        eprint("timing the CPU oracle on a bounded sample (~%.0f s)" % a.cpu_seconds)
+        cpu = cpu_baseline_encode(shape, signs, a.cpu_seconds)
+        eprint("cpu oracle: %.4g keys/s (%s)" % (cpu["value"], cpu["sample"]))
+    rec = {
+        "metric": "cached keys encoded/sec and % of HBM roofline, Hadamard/Lloyd-Max write path, B=64 T=8k",
+        "value": value, "unit": "keys/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "sweep encode: B=64 Hkv=8 d=128 b=4 T=8192, fp16 keys", "B": B, "Hkv": Hkv, "d": d,
+                   "b": b, "T": T, "k_dtype": "f16",
+                   "step": "one kvq_encode_keys call: norm, rotation, codes and norms of B*Hkv*T keys",
+                   "key_sources_rotated": len(srcs), "outputs_rotated": len(outs)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(TRAFFIC_FILE_ENC),
+                     "kernel": "hlm_encode_kernel (norm + in-register Walsh-Hadamard transform + cell-table "
+                               "code search + packing)",
+                     "avg_launch_ms": ms_per_step, "algorithmic_bytes": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
 
 
 def run_suite(K, torch, reps=5, calls=30):
@@ -402,10 +505,11 @@ def main(argv=None):
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline step, time every workload and operation (table on stderr)")
-    ap.add_argument("--variant", choices=("append", "qv", "pot"), default="append",
+    ap.add_argument("--variant", choices=("append", "qv", "pot", "encode"), default="append",
                     help="append: the fused append + decode step over fp16 V (default); qv: decode attention "
                          "with the values stored as codes of the same codec (kvq_decode_attn_qv); pot: the fused "
-                         "step with 4-bit power-of-two key codes (with the mantissa term) instead")
+                         "step with 4-bit power-of-two key codes (with the mantissa term) instead; encode: the "
+                         "write path alone at the batch-64 sweep shape (kvq_encode_keys)")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -427,6 +531,8 @@ def main(argv=None):
     if a.suite:
         run_suite(K, torch)
         return 0
+    if a.variant == "encode":
+        return run_encode(K, torch, a)
     dev = torch.device("cuda:0")
     shape = W.LONGCTX
     B, Hq, Hkv, d, T, b = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T, shape.b
