@@ -66,34 +66,6 @@ __device__ __forceinline__ void lane_signs(const uint32_t* signs, int lk, float 
   for (int j = 0; j < kEncCpl; ++j) sg[j] = ((sb >> j) & 1u) ? -1.0f : 1.0f;
 }
 
-// The butterflies from coordinate distance H0 on: in registers for distances H0 .. 8, then across the key's
-// lanes for distances 16, 32, ... (lane distances 1, 2, ...).  Across lanes the lower lane of a pair keeps
-// x + partner and the upper one partner - x, both as one fused multiply-add with +-1 (the same sums and
-// differences as the in-register stages).
-template <int D, int H0>
-__device__ __forceinline__ void butterflies_from(float (&x)[kEncCpl], int lk) {
-  constexpr int LPK = EncLanes<D>::LPK;
-#pragma unroll
-  for (int h = H0; h < kEncCpl; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < kEncCpl; ++i)
-      if ((i & h) == 0) {
-        const float a = x[i], c = x[i + h];
-        x[i] = a + c;
-        x[i + h] = a - c;
-      }
-  auto stage = [&](auto dl_tag) {
-    constexpr int DL = decltype(dl_tag)::value;
-    const float s = (lk & DL) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int j = 0; j < kEncCpl; ++j) x[j] = __builtin_fmaf(x[j], s, xor_lane<DL>(x[j]));
-  };
-  if constexpr (LPK >= 2) stage(std::integral_constant<int, 1>{});
-  if constexpr (LPK >= 4) stage(std::integral_constant<int, 2>{});
-  if constexpr (LPK >= 8) stage(std::integral_constant<int, 4>{});
-  if constexpr (LPK >= 16) stage(std::integral_constant<int, 8>{});
-}
-
 // One key is held by LPK = D/16 consecutive lanes, 16 coordinates per lane: lane lk holds coordinates
 // 16*lk .. 16*lk+15.  All LPK lanes must run the rotation together.  It leaves in x those coordinates of
 // H' D k, where H' is the unnormalised Sylvester Walsh-Hadamard matrix, and returns ||k||^2 (the same in
@@ -114,7 +86,30 @@ __device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, co
     x[i] = __builtin_fmaf(a, sg[i], c);
     x[i + 1] = __builtin_fmaf(a, sg[i], -c);
   }
-  butterflies_from<D, 2>(x, lk);
+  // remaining in-register butterflies (coordinate distances 2, 4, 8)
+#pragma unroll
+  for (int h = 2; h < kEncCpl; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < kEncCpl; ++i)
+      if ((i & h) == 0) {
+        const float a = x[i], c = x[i + h];
+        x[i] = a + c;
+        x[i + h] = a - c;
+      }
+  // cross-lane butterflies (coordinate distances 16, 32, ... = lane distances 1, 2, ...): the lower lane
+  // of a pair keeps x + partner, the upper one partner - x, both as one fused multiply-add with +-1 (the
+  // same sums and differences as the in-register stages)
+  auto stage = [&](auto dl_tag) {
+    constexpr int DL = decltype(dl_tag)::value;
+    const float s = (lk & DL) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) x[j] = __builtin_fmaf(x[j], s, xor_lane<DL>(x[j]));
+  };
+  constexpr int LPK = EncLanes<D>::LPK;
+  if constexpr (LPK >= 2) stage(std::integral_constant<int, 1>{});
+  if constexpr (LPK >= 4) stage(std::integral_constant<int, 2>{});
+  if constexpr (LPK >= 8) stage(std::integral_constant<int, 4>{});
+  if constexpr (LPK >= 16) stage(std::integral_constant<int, 8>{});
   return ss;
 }
 

@@ -81,6 +81,46 @@ def test_encode_parity(K, oracle_mod, name, shape, batches, T):
     log("  codes differing %d, tie-band coordinates %d of %d" % (n_diff, n_tie, tie.size))
 
 
+def test_encode_extreme_scales_and_non_finite_keys(K, oracle_mod):
+    """fp32 keys scaled far from 1 take the correctly rounded norm and scale (sums of squares outside
+    [2^-100, 2^100]) and still match the oracle; a key with an infinite or NaN coordinate, or whose sum of
+    squares overflows fp32, gets the middle code everywhere and its norm as computed, in the encode kernel
+    and in the fused append alike."""
+    import torch
+    shape = W.scaled(W.LLAMA8B, B=2, Hq=8, Hkv=2, T=96, dtype="f32")
+    case = make_hlm_case(shape)
+    keys = case["keys"].astype(np.float32)
+    keys[0, 0] *= np.float32(1e-18)   # sums of squares near 1e-34
+    keys[0, 1] *= np.float32(1e17)    # sums of squares near 1e36
+    keys[1, 0, :48] *= np.float32(2e-19)
+    cb = K.kvq_build_codebook(shape.d, shape.b)
+    codes, norms = _gpu_encode(K, cb, case["signs"], keys)
+    ref_codes, ref_norms, tie = oracle_cache(oracle_mod, shape, keys, case["signs"])
+    _check_codes(oracle_mod, shape, codes.cpu().numpy(), norms.cpu().numpy(), ref_codes, ref_norms, tie)
+
+    bad = np.array(keys[:1, :1, :4])
+    bad[0, 0, 0, 5] = np.inf
+    bad[0, 0, 1, 9] = np.nan
+    bad[0, 0, 2, :] = np.float32(3e38)  # the sum of squares overflows
+    bad[0, 0, 3, 0] = -np.inf
+    c_bad, n_bad = _gpu_encode(K, cb, case["signs"], bad)
+    middle = oracle_mod.unpack_codes(c_bad.cpu().numpy(), shape.d, shape.b)
+    assert np.all(middle == 1 << (shape.b - 1))
+    nb = n_bad.cpu().numpy()[0, 0]
+    assert np.isinf(nb[0]) and np.isnan(nb[1]) and np.isinf(nb[2]) and np.isinf(nb[3])
+    # the fused append encodes the same key to the same codes
+    q = torch_dev(case["q"][:1, :4])
+    cache_c = torch.zeros((1, 1, 8, cb.bytes_per_key), dtype=torch.uint8, device="cuda:0")
+    cache_n = torch.zeros((1, 1, 8), dtype=torch.float32, device="cuda:0")
+    v = torch.zeros((1, 1, 8, shape.d), dtype=torch.float16, device="cuda:0")
+    for r in range(4):
+        nk = torch_dev(np.ascontiguousarray(bad[:, :, r, :]))
+        K.kvq_decode_attn_append(cb, case["signs"], nk, q, cache_c, cache_n, v, seq_lens=torch.tensor(
+            [r + 1], dtype=torch.int32, device="cuda:0"), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cache_c[0, 0, :4].cpu().numpy(), c_bad.cpu().numpy()[0, 0])
+
+
 def test_encode_write_positions(K, oracle_mod):
     """Append at per-batch positions into a larger cache; rows outside the cache are skipped."""
     import torch
