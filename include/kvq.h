@@ -132,7 +132,10 @@ kvq_status kvq_build_codebook_pq(const float* train, int H, int64_t n, int d, in
  *   mantissa == 1:  2^-(j/2) for even j, (3/4) 2^-((j-1)/2) for odd j.
  * The element's value is alpha * (-1)^sign * magnitude(j); levels[c] holds
  * (-1)^sign * magnitude(j) for every code value c, thresholds the midpoints.
- * No rotation and no sign pattern (signs may be NULL in every call).
+ * No rotation and no sign pattern (signs may be NULL in every call).  The
+ * kernels rely on these exact levels and midpoints: every call that takes a
+ * KVQ_POT codebook returns KVQ_ERR_INVALID_ARG if a level or midpoint differs
+ * from what this function writes for (d, b, mantissa).
  *   d: power of two, 16 <= d <= 256.   b: 2..4.   mantissa: 0 or 1.
  * Errors: KVQ_ERR_INVALID_ARG for d, b, mantissa out of range or out == NULL. */
 kvq_status kvq_build_codebook_pot(int d, int b, int mantissa, kvq_codebook* out);
@@ -158,8 +161,10 @@ kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centro
  *   write_pos: device [B] int32 per-batch write positions, or NULL.
  *              Rows that would fall outside [0, T_cap) are skipped.
  *   For PQ the kv head index selects that head's centroids (Hkv == n_heads).
- * A zero key gets norm 0 and the codes of the zero vector; NaN propagates to
- * the norm (its codes are then unspecified).
+ * A zero key gets norm 0 and the codes of the zero vector.  A Hadamard/Lloyd-
+ * Max key with an infinite or NaN element, or whose sum of squares overflows
+ * fp32, gets the codes of the zero vector and its norm as computed (inf or
+ * NaN); kvq_decode_attn_append encodes such a key the same way.
  * Errors: KVQ_ERR_INVALID_ARG (sizes, NULL, misaligned, signs not +-1, t0 out
  *   of range when write_pos == NULL), KVQ_ERR_UNSUPPORTED (d, b not built),
  *   KVQ_ERR_DEVICE. */
