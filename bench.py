@@ -500,7 +500,7 @@ def main(argv=None):
     ap.add_argument("--caches", type=int, default=4, help="distinct cache copies rotated across steps")
     ap.add_argument("--splits", type=int, default=0, help="T splits (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=5.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
