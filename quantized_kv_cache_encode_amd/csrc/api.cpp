@@ -126,7 +126,12 @@ int device_cus() {
 
 // Split of the token axis: every split is a multiple of 64 tokens.  With no
 // request, aim for one workgroup per compute unit (one round of the grid) but
-// keep at least one 64-token chunk per wave in a split.
+// keep at least one 64-token chunk per wave in a split.  A launch that would
+// then fill less than half the compute units with two or more splits per unit
+// is all latency: there a split may hold half that, which halves each
+// workgroup's serial part, up to about half the compute units (beyond that,
+// and from one split to two, the merge costs more than the shorter splits
+// save).
 void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len) {
   const int64_t max_splits = (T_cap + 63) / 64;
   int64_t s;
@@ -136,7 +141,9 @@ void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, i
     const int64_t target = (int64_t)device_cus();
     s = (target + units - 1) / units;
     const int64_t min_tokens = kvq::kReadThreads;  // 64 tokens for each of the workgroup's waves
-    const int64_t cap = (T_cap + min_tokens - 1) / min_tokens;
+    int64_t cap = (T_cap + min_tokens - 1) / min_tokens;
+    if (cap > 1 && units * cap < target / 2)
+      cap = std::min((T_cap + min_tokens / 2 - 1) / (min_tokens / 2), (target / 2 + units - 1) / units);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
   }
