@@ -79,6 +79,9 @@ struct ScalarTable {
   static constexpr bool kNorm = true;
   static constexpr bool kNibbles = BITS * GRP == 4;  // rows indexed by the 4-bit fields of the packed codes
   static constexpr bool kIntLut = true;              // fixed-point table entries, summed exactly in 32-bit integers
+  // cache policy of the decode's streaming loads (codes, norms, values, new keys): non-temporal, since each
+  // byte is read once per call and by a single load
+  static constexpr int kLoadPolicy = kStreamLoad;
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) { return code_at<BITS, NW>(w, i); }
   __device__ static __forceinline__ float level_max(const float* lv) {
     float m = 0.0f;
@@ -163,6 +166,7 @@ struct PqScorer {
   static constexpr bool kNorm = false;
   static constexpr bool kNibbles = CB == 4;
   static constexpr bool kIntLut = false;
+  static constexpr int kLoadPolicy = 0;  // default policy: the non-temporal one measured slower on these small launches
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) {
     if constexpr (CB == 4) return (w[i >> 3] >> (4 * (i & 7))) & 15u;
     else return (w[i >> 2] >> (8 * (i & 3))) & 255u;
@@ -407,58 +411,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufFlags);
 }
 
-// The N-byte code row at voff + soff into little-endian 32-bit words.
-template <int N>
+// The N-byte code row at voff + soff into little-endian 32-bit words, loaded with cache policy POL.
+template <int N, int POL = 0>
 __device__ __forceinline__ void load_code_row_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&w)[(N + 3) / 4]) {
   if constexpr (N % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 16; ++k) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, POL);
       w[4 * k + 0] = x[0]; w[4 * k + 1] = x[1]; w[4 * k + 2] = x[2]; w[4 * k + 3] = x[3];
     }
   } else if constexpr (N % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 8; ++k) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff + 8 * k, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff + 8 * k, POL);
       w[2 * k + 0] = x[0]; w[2 * k + 1] = x[1];
     }
   } else if constexpr (N % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 4 * k, 0);
+    for (int k = 0; k < N / 4; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff + 4 * k, POL);
   } else {
     static_assert(N % 2 == 0, "code rows are an even number of bytes");
 #pragma unroll
     for (int k = 0; k < (N + 3) / 4; ++k) w[k] = 0;
 #pragma unroll
     for (int k = 0; k < N / 2; ++k)
-      w[k / 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff + 2 * k, 0) << (16 * (k % 2));
+      w[k / 2] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff + 2 * k, POL) << (16 * (k % 2));
   }
 }
 
 // DPL consecutive V elements (fp16 or fp32) at voff + soff: the slice this lane contributes to the MFMA
-// A operand.  Past the split's valid range the elements read as 0.
-template <typename PT, int DPL, typename VR>
+// A operand, loaded with cache policy POL.  Past the split's valid range the elements read as 0.
+template <typename PT, int DPL, typename VR, int POL = 0>
 __device__ __forceinline__ VR load_vrow_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   VR out;
   if constexpr (DPL == 1) {
     out = VR{};
-    if constexpr (sizeof(PT) == 2) out[0] = __builtin_bit_cast(PT, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
-    else out[0] = __builtin_bit_cast(PT, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    if constexpr (sizeof(PT) == 2) out[0] = __builtin_bit_cast(PT, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, POL));
+    else out[0] = __builtin_bit_cast(PT, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL));
   } else {
     constexpr int BYTES = DPL * (int)sizeof(PT);
     static_assert(BYTES == (int)sizeof(VR), "slice type");
     if constexpr (BYTES == 4) {
-      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL));
     } else if constexpr (BYTES == 8) {
-      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL));
     } else if constexpr (BYTES == 16) {
-      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+      out = __builtin_bit_cast(VR, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, POL));
     } else {
       static_assert(BYTES % 16 == 0, "V slice is a multiple of 16 bytes");
       typedef unsigned u4 __attribute__((ext_vector_type(4)));
       struct Parts { u4 x[BYTES / 16]; } parts;
 #pragma unroll
-      for (int k = 0; k < BYTES / 16; ++k) parts.x[k] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, 0);
+      for (int k = 0; k < BYTES / 16; ++k) parts.x[k] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, POL);
       out = __builtin_bit_cast(VR, parts);
     }
   }
@@ -467,22 +471,22 @@ __device__ __forceinline__ VR load_vrow_buf(__amdgpu_buffer_rsrc_t r, int voff, 
 
 // The fp16 V slice of DPL consecutive elements at voff + soff as raw 32-bit words (element e in the low
 // (e even) or high (e odd) half of word e/2; a single element sits in the low half).  Past the split's
-// valid range the words read as 0.
-template <int DPL>
+// valid range the words read as 0.  POL is the loads' cache policy.
+template <int DPL, int POL = 0>
 __device__ __forceinline__ void load_vwords_f16(__amdgpu_buffer_rsrc_t r, int voff, int soff,
                                                 uint32_t (&w)[DPL < 2 ? 1 : DPL / 2]) {
   if constexpr (DPL == 1) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, POL);
   } else if constexpr (DPL == 2) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, POL);
   } else if constexpr (DPL == 4) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, POL);
     w[0] = x[0]; w[1] = x[1];
   } else {
     static_assert(DPL % 8 == 0, "V slice is a multiple of 16 bytes");
 #pragma unroll
     for (int k = 0; k < DPL / 8; ++k) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, POL);
       w[4 * k + 0] = x[0]; w[4 * k + 1] = x[1]; w[4 * k + 2] = x[2]; w[4 * k + 3] = x[3];
     }
   }
@@ -523,6 +527,7 @@ void decode_kernel(const AttnParams p) {
   constexpr int D = S::D;
   constexpr int DPL = D / 16;  // V columns per lane per MFMA tile set
   constexpr int NT = 64 * NWV;
+  constexpr int kPol = S::kLoadPolicy;
   using Plan = LdsPlan<S, GG, NWV>;
   constexpr int HW = Plan::HW;
   using PT = typename std::conditional<VF16, _Float16, float>::type;
@@ -577,12 +582,12 @@ void decode_kernel(const AttnParams p) {
   };
   auto load_v = [&](int cc, int ks, uint32_t (&vb)[4][VW]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) load_vwords_f16<DPL>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT), vb[s]);
+    for (int s = 0; s < 4; ++s) load_vwords_f16<DPL, kPol>(rv, voff_v, (cc + 16 * ks + s) * D * (int)sizeof(PT), vb[s]);
   };
   auto fetch_codes = [&](int cc, Chunk& k) {
-    load_code_row_buf<S::BPK>(rc, voff_code, cc * S::BPK, k.w);
+    load_code_row_buf<S::BPK, kPol>(rc, voff_code, cc * S::BPK, k.w);
     k.nrm = 1.0f;
-    if constexpr (S::kNorm) k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, 0));
+    if constexpr (S::kNorm) k.nrm = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rn, lane * 4, cc * 4, kPol));
   };
   auto fetch_v = [&](int cc, Chunk& k) {
     if constexpr (kVPre) {
@@ -620,7 +625,7 @@ void decode_kernel(const AttnParams p) {
     const int ko = lane * kEncCpl * kesz;
 #pragma unroll
     for (int h = 0; h < kEncCpl / 4; ++h) {  // fp32: four 16-byte loads; fp16: two, the rest read zeros
-      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, 0);
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, kPol);
 #pragma unroll
       for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
     }
@@ -745,7 +750,7 @@ void decode_kernel(const AttnParams p) {
     } else {
 #pragma unroll 4
       for (int ks = 0; ks < 16; ++ks) {
-        const vrow_t a = load_vrow_buf<PT, DPL, vrow_t>(rv, voff_v, (cc + 4 * ks) * D * (int)sizeof(PT));
+        const vrow_t a = load_vrow_buf<PT, DPL, vrow_t, kPol>(rv, voff_v, (cc + 4 * ks) * D * (int)sizeof(PT));
         float bop = 0.0f;
         if (r16 < GG) bop = pw[r16 * kChunk + 4 * ks + kq];
 #pragma unroll

@@ -64,23 +64,25 @@ struct Field {
   static constexpr int NWIN = kExact ? NF : NF + 1;
 };
 
+// Exact fields are loaded non-temporally (each byte by one load, once per call); the windows of inexact
+// fields overlap their neighbours' words and keep the default policy, which measured faster for them.
 template <int F>
 __device__ __forceinline__ void load_field(__amdgpu_buffer_rsrc_t r, int voff, int soff, int shift,
                                            uint32_t (&f)[Field<F>::NF]) {
   if constexpr (F == 8) {
-    f[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+    f[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStreamLoad);
   } else if constexpr (F == 16) {
-    f[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+    f[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kStreamLoad);
   } else if constexpr (F == 32) {
-    f[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    f[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamLoad);
   } else if constexpr (F == 64) {
-    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamLoad);
     f[0] = x[0];
     f[1] = x[1];
   } else if constexpr (F % 128 == 0 && Field<F>::kExact) {
 #pragma unroll
     for (int k = 0; k < F / 128; ++k) {
-      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, 0);
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * k, kStreamLoad);
       f[4 * k + 0] = x[0];
       f[4 * k + 1] = x[1];
       f[4 * k + 2] = x[2];
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
 #pragma unroll
         for (int s = 0; s < 4; ++s) load_field<C::FV>(rvc, voff_v, (row + s) * C::BPK, vshift, k.vc[t][s]);
       }
-      k.kn[t] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rkn, voff_n, row * 4, 0));
-      k.vn[t] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rvn, voff_n, row * 4, 0));
+      k.kn[t] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rkn, voff_n, row * 4, kStreamLoad));
+      k.vn[t] = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rvn, voff_n, row * 4, kStreamLoad));
     }
   };
   constexpr int STR = kWaves * C::CH;

@@ -12,6 +12,13 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Non-temporal cache policy for buffer loads (the aux operand of the raw buffer-load builtins).  The decode
+// kernels use it for the cache they stream, where each byte is read once per call by a single load: the
+// long-context decode step runs 6-9 % faster with it.  Loads whose windows overlap, the scores-only kernel,
+// the small product-quantization launches and the encode keep the default policy (0), which measured as
+// fast or faster there.
+constexpr int kStreamLoad = 2;
+
 template <int N> struct VecF;
 template <> struct VecF<1> { typedef float type; };
 template <> struct VecF<2> { typedef float2 type; };
