@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
 
     const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
     if (row < 0) return;
-    store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
+    store_code_bits<BITS, true>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = nrm;
   });
 }

@@ -318,21 +318,28 @@ inline int64_t encode_keys_per_block(int64_t n_keys, int kpb) {
 }
 
 // Stores a lane's 16*BITS code bits at its byte offset lk*2*BITS of the key's code row (code rows are
-// whole multiples of 2*BITS bytes, so every store is naturally aligned).
-template <int BITS>
+// whole multiples of 2*BITS bytes, so every store is naturally aligned).  NT: non-temporal stores, for the
+// encode kernels' global code rows, which nothing reads back during the call (measured: the power-of-two
+// encode 4 % faster at the batch-64 sweep shape, the Hadamard encode unchanged within noise).
+template <int BITS, bool NT = false>
 __device__ __forceinline__ void store_code_bits(uint8_t* row, int lk, uint64_t packed) {
   uint8_t* dst = row + lk * 2 * BITS;
+  auto put = [](auto* ptr, auto v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, ptr);
+    else *ptr = v;
+  };
   if constexpr (BITS == 4) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    put(reinterpret_cast<u2v*>(dst), u2v{(uint32_t)packed, (uint32_t)(packed >> 32)});
   } else if constexpr (BITS == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = (uint32_t)packed;
+    put(reinterpret_cast<uint32_t*>(dst), (uint32_t)packed);
   } else if constexpr (BITS == 1) {
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+    put(reinterpret_cast<uint16_t*>(dst), (uint16_t)packed);
   } else {
     uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
-    d16[0] = (uint16_t)packed;
-    d16[1] = (uint16_t)(packed >> 16);
-    d16[2] = (uint16_t)(packed >> 32);
+    put(d16, (uint16_t)packed);
+    put(d16 + 1, (uint16_t)(packed >> 16));
+    put(d16 + 2, (uint16_t)(packed >> 32));
   }
 }
 

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
     const uint64_t packed = pot_encode_lane<D, BITS, MANT>(x, p.thresholds, alpha);
     const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
     if (row < 0) return;
-    store_code_bits<BITS>(p.codes + row * BPK, lk, packed);
+    store_code_bits<BITS, true>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = alpha;
   });
 }
