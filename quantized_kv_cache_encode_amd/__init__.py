@@ -11,9 +11,12 @@ __all__ = ["kvq"]
 
 
 def __getattr__(name):
+    # Only the binding and the names it defines are resolved here; anything else (the `build` submodule
+    # in particular) is left to the import system, so building never needs the library to exist.
     if name == "kvq":
         return importlib.import_module(".kvq", __name__)
-    mod = importlib.import_module(".kvq", __name__)
-    if hasattr(mod, name):
-        return getattr(mod, name)
+    if name.startswith(("kvq_", "KVQ_", "Kvq")):
+        mod = importlib.import_module(".kvq", __name__)
+        if hasattr(mod, name):
+            return getattr(mod, name)
     raise AttributeError(name)
