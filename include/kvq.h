@@ -218,6 +218,32 @@ kvq_status kvq_decode_attn(const kvq_codebook* cb, const int8_t* signs, const vo
                            void* out, kvq_dtype odtype, void* workspace, size_t ws_bytes, int n_splits,
                            void* stream);
 
+/* Size in bytes of the device array that kvq_decode_attn_noalloc uses as its
+ * workspace (one array per device, held by the library until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+/* kvq_decode_attn without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The split partials and arrival counters
+ * live in a library-owned device array of KVQ_NOALLOC_SCRATCH_BYTES bytes per
+ * device; the call allocates nothing (no hipMalloc, no hipFree).  The caller
+ * still passes every input and the output.  Arguments, layouts, results and
+ * errors are those of kvq_decode_attn (same kernels, same split choice, so the
+ * output equals kvq_decode_attn's for the same n_splits, bit for bit).
+ * The first call on a device (that device current) looks up the array's
+ * device address and clears it with a fill kernel on `stream`; every completed
+ * call leaves it ready for the next.  All calls on one device share the one
+ * array: two calls on the same device that are not ordered with respect to
+ * each other (different streams with no dependency, or host threads racing)
+ * corrupt each other's partials.
+ * Errors: those of kvq_decode_attn, and KVQ_ERR_WORKSPACE when the shape needs
+ *   more than KVQ_NOALLOC_SCRATCH_BYTES of workspace
+ *   (kvq_decode_attn_workspace(...) > KVQ_NOALLOC_SCRATCH_BYTES). */
+kvq_status kvq_decode_attn_noalloc(const kvq_codebook* cb, const int8_t* signs, const void* q, kvq_dtype qdtype,
+                                   const uint8_t* codes, const float* norms, const void* v, kvq_dtype vdtype,
+                                   int B, int Hq, int Hkv, int64_t T_cap, const int32_t* seq_lens, float scale,
+                                   void* out, kvq_dtype odtype, int n_splits, void* stream);
+
 /* One decode step in one launch: write path and read path together (AXELRAM,
  * Abstract: transform on write, table lookup on read).  For every (b, kv
  * head) the key new_keys[b][h] is encoded exactly as kvq_encode_keys does and

@@ -220,6 +220,10 @@ size_t workspace_bytes(int64_t units, int B, int Hq, int splits, int d) {
 
 }  // namespace
 
+namespace kvq {
+int set_error(int status, const char* msg) { return fail((kvq_status)status, "%s", msg); }
+}  // namespace kvq
+
 extern "C" {
 
 int kvq_version(void) { return 100; }

@@ -117,6 +117,9 @@ hipError_t launch_exact_attn(int D, const CalibParams& p, hipStream_t s);
 hipError_t launch_rel_err(const float* oh, const float* o, int64_t n, float* errors, int c, hipStream_t s);
 hipError_t launch_zero_words(uint32_t* p, size_t n_words, hipStream_t s);
 
+// Sets the calling thread's kvq_last_error() message and returns `status` (a kvq_status).
+int set_error(int status, const char* msg);
+
 // Cell grid for the encode's threshold search (codebook.cpp); false if none fits kEncodeMaxCells.
 bool choose_encode_cells(const float* thresholds, int n_thresholds, int* n_cells, float* cell_inv, float* cell_shift);
 

@@ -79,6 +79,8 @@ _lib.kvq_decode_attn.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32
                                  _P, _i32, _P, _sz, _i32, _P]
 _lib.kvq_decode_attn_append.argtypes = [_CB, _P, _P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P,
                                         _f32, _P, _i32, _P, _sz, _i32, _P]
+_lib.kvq_decode_attn_noalloc.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P, _f32,
+                                         _P, _i32, _i32, _P]
 _lib.kvq_decode_attn_qv.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32, _i32, _i64, _P, _f32, _P, _i32,
                                     _P, _sz, _i32, _P]
 _lib.kvq_select_signs_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
@@ -86,11 +88,13 @@ _lib.kvq_select_signs_workspace.restype = _sz
 _lib.kvq_select_signs.argtypes = [_CB, _P, _i32, _P, _i32, _P, _i32, _P, _i32, _i32, _i32, _i32, _i64, _f32, _P, _P,
                                   _P, _sz, _P]
 for _f in ("kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
-           "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_qv", "kvq_select_signs"):
+           "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_append", "kvq_decode_attn_qv",
+           "kvq_select_signs"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq",
-           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_append",
+           "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_noalloc",
+           "kvq_decode_attn_append",
            "kvq_decode_attn_qv", "kvq_select_signs_workspace", "kvq_select_signs")
 
 
@@ -232,6 +236,24 @@ def kvq_decode_attn(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tenso
                                 _dev(norms, "norms", torch.float32, optional=True), _dev(v, "v"), _dt(v), B, Hq, Hkv,
                                 T_cap, _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
                                 _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
+    return out
+
+
+def kvq_decode_attn_noalloc(cb: kvq_codebook, signs, q: torch.Tensor, codes: torch.Tensor, norms, v: torch.Tensor,
+                            out: torch.Tensor, scale: float | None = None, seq_lens=None, n_splits: int = 0,
+                            stream=None) -> torch.Tensor:
+    """kvq_decode_attn with the library's static scratch array as its workspace: nothing is allocated here or
+    in the library, so `out` [B][Hq][d] must be given."""
+    B, Hq, d = q.shape
+    _, Hkv, T_cap, _ = codes.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s_np, s_ptr = _signs_host(signs, d)
+    _check(_lib.kvq_decode_attn_noalloc(ctypes.byref(cb), s_ptr, _dev(q, "q"), _dt(q),
+                                        _dev(codes, "codes", torch.uint8),
+                                        _dev(norms, "norms", torch.float32, optional=True), _dev(v, "v"), _dt(v), B,
+                                        Hq, Hkv, T_cap, _dev(seq_lens, "seq_lens", torch.int32, optional=True),
+                                        float(scale), _dev(out, "out"), _dt(out), n_splits, _stream(stream)))
     return out
 
 
