@@ -32,6 +32,11 @@
  *   - codes are packed LSB-first: code i occupies bits [i*b, i*b+b) of the key's
  *     byte row, bit 0 of byte 0 first;
  *   - a zero key has norm 0 and codes of the zero vector;
+ *   - a key with an infinite or NaN element has no unit vector: it gets the
+ *     codes of the zero vector too, and its norm is what its sum of squares
+ *     gives (+inf when an element is infinite and none is NaN, NaN when an
+ *     element is NaN).  Every finite key is encoded from its exact unit vector,
+ *     however large or small its elements;
  *   - scores are raw estimates of q.k; softmax uses scale 1/sqrt(d) passed in;
  *   - grouped-query mapping: query head h reads kv head h / (Hq/Hkv);
  *   - an empty sequence (length 0) gives an all-zero attention output;
@@ -232,10 +237,15 @@ void ora_encode_keys(int d, int b, const double* thresholds, const int8_t* signs
   for (int64_t r = 0; r < n; ++r) {
     const double* k = keys + (size_t)r * d;
     double ss = 0.0;
-    for (int i = 0; i < d; ++i) ss += k[i] * k[i];
+    int finite = 1;
+    for (int i = 0; i < d; ++i) {
+      ss += k[i] * k[i];
+      if (!isfinite(k[i])) finite = 0;
+    }
     double nrm = sqrt(ss);
     norms[r] = nrm;
-    for (int i = 0; i < d; ++i) u[i] = (nrm > 0.0) ? k[i] / nrm : 0.0;
+    /* no unit vector for a zero key or one with an infinite or NaN element: y = 0 */
+    for (int i = 0; i < d; ++i) u[i] = (finite && nrm > 0.0) ? k[i] / nrm : 0.0;
     rotate(d, H, signs, u, y);
     uint8_t* row = codes + (size_t)r * bpk;
     memset(row, 0, (size_t)bpk);

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
   float sg[kEncCpl];
   lane_signs<D>(p.signs, lk, sg);
   auto code_of = [&](float y) -> uint32_t {
-    // y is finite with |y| <= 1 up to rounding (non-finite keys do not get here), and the cells span
+    // y is finite with |y| <= 1 up to rounding (keys with a non-finite coordinate do not get here), and the cells span
     // |y| <= 1.0001 with a spare cell at either end, so the cell index is in range without a clamp
     const int c = (int)__builtin_fmaf(y, p.cell_inv, p.cell_shift);
     const float2 e = cells[c];
@@ -64,10 +64,21 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
     const float ss = rotate_key_lane<D>(x, lk, sg);
     float nrm;
     const float inv = unit_scale_ss<D>(ss, nrm);
-    uint64_t packed = middle_codes<BITS>();
-    if (ss <= 0x1.fffffep127f) {  // a finite key (a NaN or infinite sum fails the test)
+    uint64_t packed;
+    if (ss <= 0x1.fffffep127f) {  // every finite key whose sum of squares stays in range
       unit_vector(x, inv);
       packed = pack_lane_codes<BITS>(x, code_of);
+    } else {  // rare: the sum overflowed, or a coordinate is infinite or NaN; the key is read again
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(keys) +
+                                                        (k * D + lk * kEncCpl) * ESZ);
+      uint32_t r2[kEncCpl];
+#pragma unroll
+      for (int h = 0; h < kEncCpl * ESZ / 16; ++h) {
+        const uint4 v = src[h];
+        r2[4 * h + 0] = v.x; r2[4 * h + 1] = v.y; r2[4 * h + 2] = v.z; r2[4 * h + 3] = v.w;
+      }
+      key_lane_floats<KF16>(r2, x);
+      packed = encode_beyond_range<D, BITS>(x, lk, sg, ss, nrm, code_of);
     }
 
     const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));

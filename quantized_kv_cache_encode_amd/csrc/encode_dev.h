@@ -113,8 +113,8 @@ __device__ __forceinline__ float rotate_key_lane(float (&x)[kEncCpl], int lk, co
   return ss;
 }
 
-// The packed bits of 16 codes of value 2^(BITS-1), the code of y = 0: what a key whose norm is not finite
-// (an infinite or NaN coordinate, or a sum of squares past the fp32 range) is given.
+// The packed bits of 16 codes of value 2^(BITS-1), the code of y = 0: what a key with an infinite or NaN
+// coordinate is given.
 template <int BITS>
 __device__ __forceinline__ uint64_t middle_codes() {
   uint64_t v = 0;
@@ -177,6 +177,34 @@ __device__ __forceinline__ uint64_t pack_lane_codes(const float (&y)[kEncCpl], Q
   return ((uint64_t)hi << 32) | lo;
 }
 
+// The rare keys whose fp32 sum of squares is not finite.  x holds the lane's coordinates as loaded (not
+// rotated), ss the key's sum of squares, and all LPK lanes of the key call this together (their ss is the
+// same).  A key with an infinite or NaN coordinate has no unit vector: it gets the code of y = 0 in every
+// coordinate and the norm sqrt(ss), +inf or NaN.  Every other such key is finite and only its sum
+// overflowed: it is rotated again from x scaled by 2^-100 (exact for every coordinate above 2^-26 of the
+// largest, and the sum then lies well inside [2^-100, 2^100]); the norm is scaled back, which rounds to
+// +inf where ||k|| itself exceeds the fp32 range.
+template <int D, int BITS, class Q>
+__device__ __forceinline__ uint64_t encode_beyond_range(float (&x)[kEncCpl], int lk, const float (&sg)[kEncCpl],
+                                                        float ss, float& nrm, Q&& code_of) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  amax = key_lanes_max<EncLanes<D>::LPK>(amax);
+  if (__builtin_isnan(ss) || !(amax <= 0x1.fffffep127f)) {
+    nrm = __builtin_sqrtf(ss);
+    return middle_codes<BITS>();
+  }
+#pragma unroll
+  for (int j = 0; j < kEncCpl; ++j) x[j] *= 0x1p-100f;
+  const float ss2 = rotate_key_lane<D>(x, lk, sg);
+  float n2;
+  const float inv = unit_scale_ss<D>(ss2, n2);
+  nrm = n2 * 0x1p100f;
+  unit_vector(x, inv);
+  return pack_lane_codes<BITS>(x, code_of);
+}
+
 // Encode of one key with the per-threshold comparison (used where a single key is encoded).  Same lane
 // layout and arithmetic as the encode kernel, whose table-driven cell search returns the same count.  raw
 // holds the lane's 16 coordinates: packed fp16 halves in raw[0..7] (kf16), else fp32 bits.
@@ -190,9 +218,14 @@ __device__ __forceinline__ uint64_t encode_key_lane(const uint32_t (&raw)[kEncCp
   lane_signs<D>(signs, lk, sg);
   const float ss = rotate_key_lane<D>(x, lk, sg);
   const float inv = unit_scale_ss<D>(ss, nrm);
-  if (!(ss <= 0x1.fffffep127f)) return middle_codes<BITS>();
+  auto code_of = [&](float y) { return code_by_count<BITS>(y, thresholds); };
+  if (!(ss <= 0x1.fffffep127f)) {  // an overflowed or non-finite sum: start again from the loaded coordinates
+    if (kf16) key_lane_floats<true>(raw, x);
+    else key_lane_floats<false>(raw, x);
+    return encode_beyond_range<D, BITS>(x, lk, sg, ss, nrm, code_of);
+  }
   unit_vector(x, inv);
-  return pack_lane_codes<BITS>(x, [&](float y) { return code_by_count<BITS>(y, thresholds); });
+  return pack_lane_codes<BITS>(x, code_of);
 }
 
 __device__ __forceinline__ int clamp_int(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }

@@ -254,6 +254,45 @@ def test_encode_zero_key(oracle_mod):
     assert np.all(oracle_mod.unpack_codes(codes, d, b) == 8)
 
 
+def test_encode_non_finite_keys(oracle_mod):
+    """Reading for keys the pages leave undefined: an infinite or NaN element leaves no unit vector, so the
+    key gets the zero key's codes (L/2 everywhere: the middle threshold of the symmetric codebook is 0 and a
+    value on a threshold takes the upper code) and its norm as its sum of squares gives it."""
+    d = 64
+    for b in (1, 2, 3, 4):
+        lv, th = oracle_mod.codebook(d, b)
+        keys = np.random.default_rng(b).standard_normal((5, d))
+        keys[0, 3] = np.inf
+        keys[1, 7] = -np.inf
+        keys[2, 0] = np.nan
+        keys[3, 1], keys[3, 2] = np.inf, np.nan
+        keys[4, :] = 0.0
+        codes, norms, _, _ = oracle_mod.encode_keys(th, W.signs(W.LONGCTX), keys, b)
+        idx = oracle_mod.unpack_codes(codes, d, b)
+        assert np.all(idx == (1 << b) // 2), b
+        assert norms[0] == np.inf and norms[1] == np.inf
+        assert np.isnan(norms[2]) and np.isnan(norms[3])
+        assert norms[4] == 0.0
+
+
+@pytest.mark.parametrize("scale_exp", [-140, -100, 100, 120])
+def test_encode_codes_are_scale_invariant_at_extreme_scales(oracle_mod, scale_exp):
+    """y = H D k / |k| does not depend on the key's scale: keys scaled by a power of two (exact in fp64) far
+    outside fp32's comfortable range (elements near 1e-42 or 1e38, sums of squares far beyond fp32) keep
+    the brute-force nearest-level codes of the unscaled keys, and their norms scale exactly."""
+    d, b = 128, 4
+    rng = np.random.default_rng(5)
+    s = (rng.integers(0, 2, d) * 2 - 1).astype(np.int8)
+    keys = rng.standard_normal((64, d))
+    lv, th = oracle_mod.codebook(d, b)
+    c0, n0, _, tie = oracle_mod.encode_keys(th, s, keys, b)
+    c1, n1, _, _ = oracle_mod.encode_keys(th, s, np.ldexp(keys, scale_exp), b)
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(n1, np.ldexp(n0, scale_exp))
+    idx, _ = _independent_codes(keys, s, lv, d)
+    np.testing.assert_array_equal(oracle_mod.unpack_codes(c1, d, b)[~tie], idx[~tie])
+
+
 def test_encode_tie_band_flags(oracle_mod):
     d, b = 16, 2
     s = np.ones(d, dtype=np.int8)
