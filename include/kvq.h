@@ -161,10 +161,12 @@ kvq_status kvq_codebook_pq(int d, int m, int K, int n_heads, const float* centro
  *   write_pos: device [B] int32 per-batch write positions, or NULL.
  *              Rows that would fall outside [0, T_cap) are skipped.
  *   For PQ the kv head index selects that head's centroids (Hkv == n_heads).
- * A zero key gets norm 0 and the codes of the zero vector.  A Hadamard/Lloyd-
- * Max key with an infinite or NaN element, or whose sum of squares overflows
- * fp32, gets the codes of the zero vector and its norm as computed (inf or
- * NaN); kvq_decode_attn_append encodes such a key the same way.
+ * A zero key gets norm 0 and the codes of the zero vector.  Every finite
+ * Hadamard/Lloyd-Max key is encoded from its unit vector whatever its scale
+ * (its fp32 norm is +inf only where |k| exceeds the fp32 range); a key with an
+ * infinite or NaN element gets the codes of the zero vector and the norm its
+ * sum of squares gives (+inf, or NaN when an element is NaN).
+ * kvq_decode_attn_append encodes every key the same way.
  * Errors: KVQ_ERR_INVALID_ARG (sizes, NULL, misaligned, signs not +-1, t0 out
  *   of range when write_pos == NULL), KVQ_ERR_UNSUPPORTED (d, b not built),
  *   KVQ_ERR_DEVICE. */
@@ -187,7 +189,10 @@ kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q,
                      const int32_t* seq_lens, float* scores, void* stream);
 
 /* Bytes of device workspace kvq_decode_attn needs for this shape and split
- * count (n_splits = 0: the library's choice).  0 on invalid arguments. */
+ * count (n_splits = 0: the library's choice).  0 on invalid arguments.  The
+ * workspace holds one arrival counter per (batch, kv head, head group) and
+ * the split partials, exchanged between workgroups as device-scope atomic
+ * words; a zero word is an empty slot. */
 size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv, int64_t T_cap, int n_splits);
 
 /* Fused decode attention from codes (AXELRAM, Abstract: scores by table
@@ -201,12 +206,12 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
  *   out:      device [B][Hq][d], dtype odtype, written.  A sequence of
  *             length 0 gives zeros.
  *   workspace: device, at least kvq_decode_attn_workspace(...) bytes with the
- *             same n_splits (may be NULL when that size is 0).  Its first
- *             bytes are arrival counters that must be zero before the first
- *             call using this workspace (allocate it zero-filled); every
- *             completed call leaves them zero again, so the workspace can be
- *             reused by later calls ordered on the device without clearing.
- *             Calls that share a workspace concurrently race.
+ *             same n_splits (may be NULL when that size is 0).  All of it must
+ *             be zero before the first call using this workspace (allocate it
+ *             zero-filled); every completed call leaves it zero again, so the
+ *             workspace can be reused by later calls ordered on the device,
+ *             with any shape, without clearing.  Calls that share a workspace
+ *             concurrently race.
  *   n_splits: 0 = library's choice; otherwise 1..T_cap/64 rounded up (the
  *             result is the same up to rounding for every n_splits).
  * Errors: as kvq_encode_keys, plus KVQ_ERR_WORKSPACE, and KVQ_ERR_UNSUPPORTED

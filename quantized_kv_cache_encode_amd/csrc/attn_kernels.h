@@ -30,8 +30,10 @@
 //   16x16x4 f32) whose A operand is V^T, giving out^T[dim][head] in the
 //   matrix-core accumulators.  The waves merge their (max, sum, acc)
 //   through LDS; the splits of one (b, kv head, head group) are merged by
-//   the last of its workgroups to finish (log-sum-exp merge), found with an
-//   arrival counter in the workspace that the last workgroup resets to zero.
+//   the last of its workgroups to finish (log-sum-exp merge), elected by an
+//   arrival counter in the workspace that it resets to zero; the partials
+//   travel as device-scope atomic words that are never zero, so the merger
+//   reads each word until it has been written and then clears it.
 #pragma once
 
 #include <type_traits>
@@ -48,7 +50,7 @@ constexpr int kChunk = 64;
 constexpr float kLazyHeadroom = 8.0f;  // log2 of the largest probability allowed before rescaling
 constexpr int kMaxSplits = 256;        // T splits per (b, kv head, head group)
 constexpr int kRecPad = 4;             // split partial record = D accumulators + max + sum, padded to D + 4
-constexpr int kMergeTile = 32;         // splits whose partials the merging workgroup loads at once
+constexpr int kMergeTile = 8;          // splits whose partials the merging workgroup loads at once
 
 template <int B, int NW>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int i) {
@@ -194,22 +196,34 @@ struct PqScorer {
   }
 };
 
-template <class S, int GG, int NWV = kWaves>
+// LDS layout of the read kernels.  kRec: the decode kernels' per-wave records (accumulators padded to RS floats
+// per row, maxima, sums) and the workgroup's merged partials; they get a region of their own when the whole
+// layout still fits comfortably in the 160 KB of LDS (so a wave can write its record as soon as its loop
+// ends), else they reuse the table's space once every wave is done with it.
+template <class S, int GG, int NWV = kWaves, bool kRec = true>
 struct LdsPlan {
   static constexpr int HW = GG < 4 ? GG : 4;
   static constexpr int NQ = GG / HW;
+  static constexpr int RS = S::D + 4;
   static constexpr size_t lut_bytes = (size_t)GG * S::ROWS * S::COLS * 4;
-  static constexpr size_t red_bytes = (size_t)NWV * GG * (S::D + 2) * 4;
-  static constexpr size_t region0 = ((lut_bytes > red_bytes ? lut_bytes : red_bytes) + 15) / 16 * 16;
+  static constexpr size_t lut_al = (lut_bytes + 15) / 16 * 16;
+  static constexpr size_t red_bytes = kRec ? (size_t)NWV * GG * (RS + 2) * 4 + (size_t)GG * (S::D + 2) * 4 : 0;
+  static constexpr bool kRedSeparate = kRec && lut_al + red_bytes + 48 * 1024 <= 160 * 1024;
+  static constexpr size_t red_off = kRedSeparate ? lut_al : 0;
+  static constexpr size_t red_end = red_off + red_bytes;
+  static constexpr size_t region0 = ((red_end > lut_bytes ? red_end : lut_bytes) + 15) / 16 * 16;
   // consts: 16 levels (+0), merge flag (+96), per-wave progress (+128, up to 16 waves), appended key's codes
-  // (+192) and norm (+320)
+  // (+192), its norm (+320) and its ready flag (+324)
   static constexpr size_t consts_off = region0;
   static constexpr size_t newcode_off = consts_off + 192;
   static constexpr size_t newnorm_off = consts_off + 320;
   static constexpr size_t qs_off = consts_off + 336;              // GG * D floats
   static constexpr size_t qa_off = qs_off + (size_t)GG * S::D * 4;  // GG floats: sum_i |q'_{g,i}|
   static constexpr size_t pst_off = qa_off + 32;
-  static constexpr size_t pst_bytes(bool f16) { return (size_t)NWV * GG * kChunk * (f16 ? 2 : 4); }
+  // probability staging rows, padded so that the GG rows a matrix-core operand read touches fall in
+  // different LDS banks: fp16 rows 72 halves (36 words) apart, fp32 rows 68 words apart
+  static constexpr int pst_row(bool f16) { return kChunk + (f16 ? 8 : 4); }
+  static constexpr size_t pst_bytes(bool f16) { return (size_t)NWV * GG * pst_row(f16) * (f16 ? 2 : 4); }
   static constexpr size_t total(bool f16) { return pst_off + pst_bytes(f16); }
 };
 
@@ -503,20 +517,137 @@ __device__ __forceinline__ half4_t gather_col_f16(const uint32_t (&r0)[VW], cons
   return __builtin_bit_cast(half4_t, x);
 }
 
-// Arrival counter of one (b, kv head, head group): zero before the call, incremented once by every
-// split's workgroup (a single device-scope fetch-add: no retry loop, so late arrivals do not queue behind
-// each other), and put back to zero by the last one, which merges the splits.
-__device__ __forceinline__ unsigned arrive(unsigned* c) {
-  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+// ---- split merge across the workgroups of one (b, kv head, head group)
+//
+// Each split's workgroup counts itself in on an arrival counter once its own loop and wave merge are done;
+// the last one to arrive merges every split (log-sum-exp) and puts the counter back to zero.  Since every
+// other workgroup has arrived by then, and publishes its partials without waiting for anything, the merger
+// may simply read each partial until it is there.  The partials are 32-bit device-scope atomic words
+// (relaxed: each word carries its own value, so no fence and no cache maintenance is needed; device-scope
+// accesses reach the coherence point shared by all XCDs).  A word is the value's bits with the sign bit
+// flipped and a negative zero stored as +0, so a written word is never 0: the workspace starts zeroed, a
+// zero word is an empty slot, and the merger clears every slot it has read, leaving the workspace zeroed for
+// the next call.  Record of split s of query-head row r: words [D sums, max, total, pad] at
+// ws + (r * n_splits + s) * (D + kRecPad).
+
+__device__ __forceinline__ uint32_t enc_word(float x) {
+  uint32_t b = __builtin_bit_cast(uint32_t, x);
+  if (b == 0x80000000u) b = 0u;
+  return b ^ 0x80000000u;
+}
+__device__ __forceinline__ float dec_word(uint32_t w) { return __builtin_bit_cast(float, w ^ 0x80000000u); }
+__device__ __forceinline__ void st_word(uint32_t* p, uint32_t w) {
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_word(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// a word that is still 0 has not landed yet; its writer has arrived, so it will
+__device__ __forceinline__ uint32_t await_word(const uint32_t* p, uint32_t w) {
+  while (w == 0u) {
+    __builtin_amdgcn_s_sleep(2);
+    w = ld_word(p);
+  }
+  return w;
 }
 
-// Split partials are exchanged between workgroups (possibly on different XCDs, whose L2 caches are not
-// coherent with each other) with device-scope stores and loads, which go to the device coherence point
-// instead of a non-coherent cache; a writer waits for its stores to complete before it counts itself in.
-__device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Counts this workgroup in (one device-scope fetch-add, no retry loop) and tells whether it is the last of
+// the n_splits, which then merges them; the last one resets the counter for the next call.
+__device__ __forceinline__ bool elect_merger(unsigned* c, int n_splits) {
+  const unsigned t = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = t + 1u == (unsigned)n_splits;
+  if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
 }
+
+// Element dc of this split's partials (and, for dc == 0, the head's running maximum and total).
+template <int D>
+__device__ __forceinline__ void publish_partial(uint32_t* rec, int dc, float num, float M, float den) {
+  st_word(rec + dc, enc_word(num));
+  if (dc == 0) {
+    st_word(rec + D, enc_word(M));
+    st_word(rec + D + 1, enc_word(den));
+  }
+}
+
+// The merger's log-sum-exp of element dc over every split of one query-head row, folded in split order (so
+// the result does not depend on which workgroup merges): its own split `own` from (M, num, den), the others
+// from their records at base, loads of kMergeTile splits issued together.  Returns the merged maximum, sum
+// and total in M, num, den.
+template <int D>
+__device__ __forceinline__ void merge_partials(const uint32_t* base, int n_splits, int own, int dc, float& M,
+                                               float& num, float& den) {
+  const float own_m = M, own_n = num, own_d = den;
+  M = -INFINITY;
+  num = den = 0.0f;
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeTile) {
+    uint32_t mw[kMergeTile], dw[kMergeTile], nw[kMergeTile];
+#pragma unroll
+    for (int k = 0; k < kMergeTile; ++k) {
+      mw[k] = dw[k] = nw[k] = 1u;
+      if (s0 + k < n_splits && s0 + k != own) {
+        const uint32_t* rec = base + (size_t)(s0 + k) * (D + kRecPad);
+        mw[k] = ld_word(rec + D);
+        dw[k] = ld_word(rec + D + 1);
+        nw[k] = ld_word(rec + dc);
+      }
+    }
+    float mv[kMergeTile], dv[kMergeTile], nv[kMergeTile];
+#pragma unroll
+    for (int k = 0; k < kMergeTile; ++k) {
+      mv[k] = -INFINITY;
+      dv[k] = nv[k] = 0.0f;
+      if (s0 + k == own) {
+        mv[k] = own_m;
+        dv[k] = own_d;
+        nv[k] = own_n;
+      } else if (s0 + k < n_splits) {
+        const uint32_t* rec = base + (size_t)(s0 + k) * (D + kRecPad);
+        mv[k] = dec_word(await_word(rec + D, mw[k]));
+        dv[k] = dec_word(await_word(rec + D + 1, dw[k]));
+        nv[k] = dec_word(await_word(rec + dc, nw[k]));
+      }
+    }
+    float Mt = M;
+#pragma unroll
+    for (int k = 0; k < kMergeTile; ++k) Mt = fmaxf(Mt, mv[k]);
+    if (Mt == -INFINITY) continue;
+    const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mt);
+    num *= f;
+    den *= f;
+#pragma unroll
+    for (int k = 0; k < kMergeTile; ++k) {
+      const float wt = mv[k] == -INFINITY ? 0.0f : fast_exp2(mv[k] - Mt);
+      num += wt * nv[k];
+      den += wt * dv[k];
+    }
+    M = Mt;
+  }
+}
+
+// Clears the words of element dc (and, for dc == 0, the maximum and total) of every split but `own`, whose
+// record the merger never wrote.  Called once every thread of the merger has read its words.
+template <int D>
+__device__ __forceinline__ void clear_partials(uint32_t* base, int n_splits, int own, int dc) {
+  for (int s2 = 0; s2 < n_splits; ++s2) {
+    if (s2 == own) continue;
+    uint32_t* rec = base + (size_t)s2 * (D + kRecPad);
+    st_word(rec + dc, 0u);
+    if (dc == 0) {
+      st_word(rec + D, 0u);
+      st_word(rec + D + 1, 0u);
+    }
+  }
+}
+
+// Per-wave progress counters in LDS, read and written with workgroup-scope relaxed atomics.  They must stay
+// LDS accesses: a volatile access through a generic pointer compiles to a flat access, whose completion wait
+// also waits for every outstanding global load of the wave (the prefetched chunk included).
+struct WaveProgress {
+  int* p;
+  __device__ int get(int w) const { return __hip_atomic_load(p + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
+  __device__ void set(int w, int v) const { __hip_atomic_store(p + w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); }
+};
 
 // NWV waves per workgroup: 8 (two per SIMD), or 12 (three per SIMD, for d = 64 with fp16 V and long splits:
 // the third wave hides more latency, paid for with a shallower gather pipeline and V requested when its
@@ -535,9 +666,10 @@ void decode_kernel(const AttnParams p) {
   __shared__ __align__(16) unsigned char smem[Plan::total(VF16)];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
   int* s_flag = reinterpret_cast<int*>(smem + Plan::consts_off + 96);
-  volatile int* s_prog = reinterpret_cast<int*>(smem + Plan::consts_off + 128);  // [NWV] chunks done
+  const WaveProgress s_prog{reinterpret_cast<int*>(smem + Plan::consts_off + 128)};  // [NWV] chunks done
   uint32_t* s_newc = reinterpret_cast<uint32_t*>(smem + Plan::newcode_off);
   float* s_newn = reinterpret_cast<float*>(smem + Plan::newnorm_off);
+  int* s_newready = reinterpret_cast<int*>(smem + Plan::newnorm_off + 4);
   static_assert(S::NW * 4 <= 128, "appended key's codes fit their LDS slot");
   float* qs = reinterpret_cast<float*>(smem + Plan::qs_off);
   float* qa = reinterpret_cast<float*>(smem + Plan::qa_off);
@@ -603,58 +735,68 @@ void decode_kernel(const AttnParams p) {
   Chunk ka, kb;
 
   // Fused append (the scalar codecs): the workgroup whose split holds the sequence's last position
-  // encodes the new key itself -- wave 1, D/16 lanes, with the arithmetic of the encode kernel -- keeps its
-  // codes and norm in LDS for its own scores, and (head group 0 only) writes them to the cache.  Every
-  // wave issues the key load; it reads zeros except in the encoding lanes, so it needs no branch.
+  // encodes the new key itself -- its last wave, which has the fewest chunks of the split, D/16 lanes, with
+  // the arithmetic of the encode kernel, after the table is built (so the encode holds up no other wave) --
+  // keeps its codes and norm in LDS for the wave that scores that position, and (head group 0 only) writes
+  // them to the cache.
   constexpr int LPK = EncLanes<D>::LPK;
+  constexpr int kEncWave = NWV - 1;
   const bool app = S::kIntLut && p.new_keys != nullptr && n_valid > 0 && u.len <= t_begin + p.split_len;
   const int rel = n_valid - 1;  // the new key's position within the split, when app
-  const bool enc_lanes = app && wid == 1 && lane < LPK;
+  const bool enc_lanes = app && wid == kEncWave && lane < LPK;
   const int64_t new_row = (int64_t)u.b * p.Hkv + u.kvh;
   const int kesz = p.new_f16 ? 2 : 4;
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(app ? (const void*)(reinterpret_cast<const char*>(p.new_keys) + new_row * D * kesz) : p.codes,
-                app && wid == 1 ? D * kesz : 0);
-  uint32_t kraw[kEncCpl];  // the lane's 16 coordinates of the new key (fp16 in the first 8 words)
+                app && wid == kEncWave ? D * kesz : 0);
 
   // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
   // burst streams in while the queries are rotated and the table is built.
   prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] {
     fetch_codes(c, ka);
     fetch_v(c, ka);
-    const int ko = lane * kEncCpl * kesz;
-#pragma unroll
-    for (int h = 0; h < kEncCpl / 4; ++h) {  // fp32: four 16-byte loads; fp16: two, the rest read zeros
-      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, kPol);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
-    }
   });
+  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  if (lane == 0) s_prog.set(wid, 0);
+  if (tid == 0) *s_newready = 0;
+  lds_barrier();
   if constexpr (S::kIntLut) {
-    if (enc_lanes) {
-      float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
-      uint64_t packed;
-      if constexpr (S::kRotate) {
-        packed = encode_key_lane<D, S::CODE_BITS>(kraw, p.new_f16 != 0, lane, p.signs, p.thresholds, nrm);
-      } else {
-        float x[kEncCpl];
-        if (p.new_f16) key_lane_floats<true>(kraw, x);
-        else key_lane_floats<false>(kraw, x);
-        packed = p.pot_mant ? pot_encode_lane<D, S::CODE_BITS, true>(x, p.thresholds, nrm)
-                           : pot_encode_lane<D, S::CODE_BITS, false>(x, p.thresholds, nrm);
+    if (app && wid == kEncWave) {
+      // the lane's 16 coordinates of the new key (fp16 in the first 8 words): four 16-byte loads for fp32,
+      // two for fp16 (the rest read zeros), nonzero in the encoding lanes only
+      uint32_t kraw[kEncCpl];
+      const int ko = lane * kEncCpl * kesz;
+#pragma unroll
+      for (int h = 0; h < kEncCpl / 4; ++h) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, kPol);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
       }
-      store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
-      if (lane == 0) *s_newn = nrm;
-      if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)
-        const int64_t row = new_row * p.T_cap + (u.len - 1);
-        store_code_bits<S::CODE_BITS>(p.app_codes + row * S::BPK, lane, packed);
-        if (lane == 0) p.app_norms[row] = nrm;
+      if (enc_lanes) {
+        float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
+        uint64_t packed;
+        if constexpr (S::kRotate) {
+          packed = encode_key_lane<D, S::CODE_BITS>(kraw, p.new_f16 != 0, lane, p.signs, p.thresholds, nrm);
+        } else {
+          float x[kEncCpl];
+          if (p.new_f16) key_lane_floats<true>(kraw, x);
+          else key_lane_floats<false>(kraw, x);
+          packed = p.pot_mant ? pot_encode_lane<D, S::CODE_BITS, true>(x, p.thresholds, nrm)
+                             : pot_encode_lane<D, S::CODE_BITS, false>(x, p.thresholds, nrm);
+        }
+        store_code_bits<S::CODE_BITS>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
+        if (lane == 0) *s_newn = nrm;
+        if (blockIdx.y % p.n_groups == 0) {  // one writer per (b, kv head)
+          const int64_t row = new_row * p.T_cap + (u.len - 1);
+          store_code_bits<S::CODE_BITS>(p.app_codes + row * S::BPK, lane, packed);
+          if (lane == 0) p.app_norms[row] = nrm;
+        }
       }
+      // publish the codes and norm in LDS to the wave that scores the new position
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) __hip_atomic_store(s_newready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
-  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
-  if (lane == 0) s_prog[wid] = 0;
-  lds_barrier();
   // softmax argument of head g per unit of table sum and of key norm: scale * log2(e) (* 2^-e_g)
   float hz[GG];
 #pragma unroll
@@ -672,12 +814,17 @@ void decode_kernel(const AttnParams p) {
   float4_t oacc[DPL];
 #pragma unroll
   for (int j = 0; j < DPL; ++j) oacc[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  PT* pw = pst + wid * GG * kChunk;
+  constexpr int PST = Plan::pst_row(VF16);
+  PT* pw = pst + wid * GG * PST;
   int done = 0;  // chunks this wave has processed
 
   // score one chunk (keys cc .. cc+63 of the split) and fold it into the softmax state and the output
   auto process = [&](int cc, Chunk& k) {
     if (app && cc <= rel && rel < cc + kChunk) {  // the appended key: codes and norm from LDS
+      // written by the encoding wave right after the table barrier; it waits for nothing, so this ends
+      while (__hip_atomic_load(s_newready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       if (lane == rel - cc) {
 #pragma unroll
         for (int kk = 0; kk < S::NW; ++kk) k.w[kk] = s_newc[kk];
@@ -724,7 +871,7 @@ void decode_kernel(const AttnParams p) {
     for (int g = 0; g < GG; ++g) {
       const float pr = fast_exp2(z[g] - m_run[g]);
       l_lane[g] += pr;
-      pw[g * kChunk + lane] = (PT)pr;
+      pw[g * PST + lane] = (PT)pr;
     }
     wave_lds_sync();
 
@@ -733,7 +880,7 @@ void decode_kernel(const AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         half4_t bop = half4_t{0, 0, 0, 0};
-        if (r16 < GG) bop = *reinterpret_cast<const half4_t*>(pw + r16 * kChunk + 16 * ks + 4 * kq);
+        if (r16 < GG) bop = *reinterpret_cast<const half4_t*>(pw + r16 * PST + 16 * ks + 4 * kq);
         uint32_t vl[kVPre || kVChunk ? 1 : 4][VW];  // d = 256: four slices loaded here
         if constexpr (!kVPre && !kVChunk) load_v(cc, ks, vl);
         const auto& vb = [&]() -> const uint32_t(&)[4][VW] {
@@ -752,7 +899,7 @@ void decode_kernel(const AttnParams p) {
       for (int ks = 0; ks < 16; ++ks) {
         const vrow_t a = load_vrow_buf<PT, DPL, vrow_t, kPol>(rv, voff_v, (cc + 4 * ks) * D * (int)sizeof(PT));
         float bop = 0.0f;
-        if (r16 < GG) bop = pw[r16 * kChunk + 4 * ks + kq];
+        if (r16 < GG) bop = pw[r16 * PST + 4 * ks + kq];
 #pragma unroll
         for (int j = 0; j < DPL; ++j) oacc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], bop, oacc[j], 0, 0, 0);
       }
@@ -763,11 +910,11 @@ void decode_kernel(const AttnParams p) {
     // older wave, which would otherwise finish well before its partners and leave the SIMD partly idle for
     // the rest of the split.  A wave that is ahead of the slowest of its partners drops its priority.
     ++done;
-    if (lane == 0) s_prog[wid] = done;
-    int other = __builtin_amdgcn_readfirstlane(s_prog[(wid + 4) % NWV]);
+    if (lane == 0) s_prog.set(wid, done);
+    int other = __builtin_amdgcn_readfirstlane(s_prog.get((wid + 4) % NWV));
 #pragma unroll
     for (int k = 2; k < NWV / 4; ++k) {
-      const int o = __builtin_amdgcn_readfirstlane(s_prog[(wid + 4 * k) % NWV]);
+      const int o = __builtin_amdgcn_readfirstlane(s_prog.get((wid + 4 * k) % NWV));
       other = o < other ? o : other;
     }
     if (done > other) __builtin_amdgcn_s_setprio(0);
@@ -782,20 +929,34 @@ void decode_kernel(const AttnParams p) {
     process(c + STR, kb);
   }
 
-  // ---- merge the four waves through LDS (the table is no longer needed)
+  // ---- merge the waves' records (max, total, sums) through LDS
   float l_w[GG];
 #pragma unroll
   for (int g = 0; g < GG; ++g) l_w[g] = wave_sum(l_lane[g]);
   __builtin_amdgcn_s_setprio(0);
-  lds_barrier();  // every wave is done with the table, whose space now holds the per-wave partials
-  float* red = reinterpret_cast<float*>(smem);            // [NWV][GG][D]
-  float* red_m = red + NWV * GG * D;                       // [NWV][GG]
-  float* red_l = red_m + NWV * GG;                         // [NWV][GG]
+  constexpr int RS = Plan::RS;
+  float* red = reinterpret_cast<float*>(smem + Plan::red_off);  // [NWV][GG][RS]
+  float* red_m = red + NWV * GG * RS;                           // [NWV][GG]
+  float* red_l = red_m + NWV * GG;                              // [NWV][GG]
+  float* mine = red_l + NWV * GG;                               // [GG][D] the workgroup's merged sums
+  float* mine_m = mine + GG * D;                                // [GG]
+  float* mine_d = mine_m + GG;                                  // [GG]
+  if constexpr (!Plan::kRedSeparate) lds_barrier();  // the records overwrite the table
   if (r16 < GG) {
+    // the lane's 4 DPL sums are dims DPL (4 kq + r) + j: one contiguous run, written as 16-byte vectors
+    float* dst = red + (wid * GG + r16) * RS + DPL * 4 * kq;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j)
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (DPL % 4 == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[(wid * GG + r16) * D + DPL * (4 * kq + r) + j] = oacc[j][r];
+        for (int j0 = 0; j0 < DPL; j0 += 4)
+          *reinterpret_cast<float4*>(dst + DPL * r + j0) =
+              make_float4(oacc[j0][r], oacc[j0 + 1][r], oacc[j0 + 2][r], oacc[j0 + 3][r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) dst[DPL * r + j] = oacc[j][r];
+      }
+    }
   }
 #pragma unroll
   for (int g = 0; g < GG; ++g)
@@ -804,6 +965,8 @@ void decode_kernel(const AttnParams p) {
       red_l[wid * GG + g] = l_w[g];
     }
   lds_barrier();
+  const bool split_merge = p.n_splits > 1;
+  if (split_merge && tid == 0) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
   for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
@@ -814,81 +977,55 @@ void decode_kernel(const AttnParams p) {
 #pragma unroll
       for (int w2 = 0; w2 < NWV; ++w2) {
         const float wt = fast_exp2(red_m[w2 * GG + g] - M);
-        num += wt * red[(w2 * GG + g) * D + dc];
+        num += wt * red[(w2 * GG + g) * RS + dc];
         den += wt * red_l[w2 * GG + g];
       }
     }
-    const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
-    if (p.n_splits == 1) {
+    if (!split_merge) {
+      const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
       const float o = den > 0.0f ? num / den : 0.0f;
       if (p.out_f16) reinterpret_cast<_Float16*>(p.out)[row * D + dc] = (_Float16)o;
       else reinterpret_cast<float*>(p.out)[row * D + dc] = o;
     } else {
-      float* dst = p.ws + (row * p.n_splits + split) * (D + kRecPad);
-      st_dev(dst + dc, num);
+      mine[idx] = num;
       if (dc == 0) {
-        st_dev(dst + D, M);
-        st_dev(dst + D + 1, den);
+        mine_m[g] = M;
+        mine_d[g] = den;
       }
     }
   }
-  if (p.n_splits == 1) return;
+  if (!split_merge) return;
 
-  // ---- the last workgroup of this (b, kv head, head group) to arrive merges all splits
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const bool last = arrive(p.counters + blockIdx.y) == (unsigned)p.n_splits;
-    if (last) __hip_atomic_store(p.counters + blockIdx.y, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_flag = last;
-  }
-  __syncthreads();
-  if (!*s_flag) return;
-  const int S_ = p.n_splits;
+  // ---- split merge: every workgroup but the last publishes its partials; the last merges all splits
+  lds_barrier();
+  const bool last = *s_flag;
+  uint32_t* wsw = reinterpret_cast<uint32_t*>(p.ws);
   for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
-    const float* base = p.ws + row * (size_t)S_ * (D + kRecPad);
-    // online log-sum-exp merge over tiles of kMergeTile splits; each tile's loads are issued together
-    float M = -INFINITY, num = 0.0f, den = 0.0f;
-    for (int s0 = 0; s0 < S_; s0 += kMergeTile) {
-      float mv[kMergeTile], dv[kMergeTile], nv[kMergeTile];
-#pragma unroll
-      for (int k = 0; k < kMergeTile; ++k) {
-        mv[k] = -INFINITY;
-        dv[k] = 0.0f;
-        nv[k] = 0.0f;
-        if (s0 + k < S_) {
-          const float* rec = base + (size_t)(s0 + k) * (D + kRecPad);
-          mv[k] = ld_dev(rec + D);
-          dv[k] = ld_dev(rec + D + 1);
-          nv[k] = ld_dev(rec + dc);
-        }
-      }
-      float Mt = M;
-#pragma unroll
-      for (int k = 0; k < kMergeTile; ++k) Mt = fmaxf(Mt, mv[k]);
-      if (Mt == -INFINITY) continue;
-      const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mt);
-      num *= f;
-      den *= f;
-#pragma unroll
-      for (int k = 0; k < kMergeTile; ++k) {
-        const float wt = mv[k] == -INFINITY ? 0.0f : fast_exp2(mv[k] - Mt);
-        num += wt * nv[k];
-        den += wt * dv[k];
-      }
-      M = Mt;
+    uint32_t* base = wsw + row * (size_t)p.n_splits * (D + kRecPad);
+    float M = mine_m[g], num = mine[idx], den = mine_d[g];
+    if (!last) {
+      publish_partial<D>(base + (size_t)split * (D + kRecPad), dc, num, M, den);
+      continue;
     }
+    merge_partials<D>(base, p.n_splits, split, dc, M, num, den);
     const float o = den > 0.0f ? num / den : 0.0f;
     if (p.out_f16) reinterpret_cast<_Float16*>(p.out)[row * D + dc] = (_Float16)o;
     else reinterpret_cast<float*>(p.out)[row * D + dc] = o;
+  }
+  if (!last) return;
+  __syncthreads();  // every thread of the merger has read its words
+  for (int idx = tid; idx < GG * D; idx += NT) {
+    const int g = idx / D, dc = idx % D;
+    const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
+    clear_partials<D>(wsw + row * (size_t)p.n_splits * (D + kRecPad), p.n_splits, split, dc);
   }
 }
 
 template <class S, int GG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_kernel(const AttnParams p) {
-  using Plan = LdsPlan<S, GG>;
+  using Plan = LdsPlan<S, GG, kWaves, false>;
   constexpr int HW = Plan::HW;
   __shared__ __align__(16) unsigned char smem[Plan::pst_off];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
@@ -990,10 +1127,10 @@ hipError_t run_decode(int gg, bool v_f16, const AttnParams& p, dim3 grid, hipStr
 template <class S>
 hipError_t run_score(int gg, const AttnParams& p, dim3 grid, hipStream_t s) {
   switch (gg) {
-    case 1: return launch_attn(score_kernel<S, 1>, LdsPlan<S, 1>::pst_off, grid, s, p);
-    case 2: return launch_attn(score_kernel<S, 2>, LdsPlan<S, 2>::pst_off, grid, s, p);
-    case 4: return launch_attn(score_kernel<S, 4>, LdsPlan<S, 4>::pst_off, grid, s, p);
-    case 8: return launch_attn(score_kernel<S, 8>, LdsPlan<S, 8>::pst_off, grid, s, p);
+    case 1: return launch_attn(score_kernel<S, 1>, LdsPlan<S, 1, kWaves, false>::pst_off, grid, s, p);
+    case 2: return launch_attn(score_kernel<S, 2>, LdsPlan<S, 2, kWaves, false>::pst_off, grid, s, p);
+    case 4: return launch_attn(score_kernel<S, 4>, LdsPlan<S, 4, kWaves, false>::pst_off, grid, s, p);
+    case 8: return launch_attn(score_kernel<S, 8>, LdsPlan<S, 8, kWaves, false>::pst_off, grid, s, p);
     default: return hipErrorNotSupported;
   }
 }

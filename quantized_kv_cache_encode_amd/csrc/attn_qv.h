@@ -503,6 +503,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
   }
   lds_barrier();
+  const bool split_merge = p.n_splits > 1;
+  float* mine_m = qs;       // [GG] this workgroup's merged maxima and totals (the rotated queries are no
+  float* mine_d = qs + GG;  // longer needed); its merged sums go to xs
+  if (split_merge && tid == 0) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
   for (int idx = tid; idx < GG * D; idx += kThreads) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
@@ -517,65 +521,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
         den += wt * red_l[w2 * GG + g];
       }
     }
-    if (p.n_splits == 1) {
+    if (!split_merge) {
       xs[idx] = den > 0.0f ? num / den : 0.0f;
     } else {
-      const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
-      float* dst = p.ws + (row * p.n_splits + split) * (D + kRecPad);
-      st_dev(dst + dc, num);
+      xs[idx] = num;
       if (dc == 0) {
-        st_dev(dst + D, M);
-        st_dev(dst + D + 1, den);
+        mine_m[g] = M;
+        mine_d[g] = den;
       }
     }
   }
-  if (p.n_splits > 1) {
-    // ---- the last workgroup of this (b, kv head, head group) to arrive merges all splits
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (tid == 0) {
-      const bool last = arrive(p.counters + blockIdx.y) == (unsigned)p.n_splits;
-      if (last) __hip_atomic_store(p.counters + blockIdx.y, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      *s_flag = last;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
-    const int S_ = p.n_splits;
+  if (split_merge) {
+    // ---- every workgroup but the last publishes its partials; the last merges all splits
+    lds_barrier();
+    const bool last = *s_flag;
+    uint32_t* wsw = reinterpret_cast<uint32_t*>(p.ws);
     for (int idx = tid; idx < GG * D; idx += kThreads) {
       const int g = idx / D, dc = idx % D;
       const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
-      const float* base = p.ws + row * (size_t)S_ * (D + kRecPad);
-      float M = -INFINITY, num = 0.0f, den = 0.0f;
-      for (int s0 = 0; s0 < S_; s0 += kMergeTile) {
-        float mv[kMergeTile], dv[kMergeTile], nv[kMergeTile];
-#pragma unroll
-        for (int k = 0; k < kMergeTile; ++k) {
-          mv[k] = -INFINITY;
-          dv[k] = 0.0f;
-          nv[k] = 0.0f;
-          if (s0 + k < S_) {
-            const float* rec = base + (size_t)(s0 + k) * (D + kRecPad);
-            mv[k] = ld_dev(rec + D);
-            dv[k] = ld_dev(rec + D + 1);
-            nv[k] = ld_dev(rec + dc);
-          }
-        }
-        float Mt = M;
-#pragma unroll
-        for (int k = 0; k < kMergeTile; ++k) Mt = fmaxf(Mt, mv[k]);
-        if (Mt == -INFINITY) continue;
-        const float f = M == -INFINITY ? 0.0f : fast_exp2(M - Mt);
-        num *= f;
-        den *= f;
-#pragma unroll
-        for (int k = 0; k < kMergeTile; ++k) {
-          const float wt = mv[k] == -INFINITY ? 0.0f : fast_exp2(mv[k] - Mt);
-          num += wt * nv[k];
-          den += wt * dv[k];
-        }
-        M = Mt;
+      uint32_t* base = wsw + row * (size_t)p.n_splits * (D + kRecPad);
+      float M = mine_m[g], num = xs[idx], den = mine_d[g];
+      if (!last) {
+        publish_partial<D>(base + (size_t)split * (D + kRecPad), dc, num, M, den);
+        continue;
       }
+      merge_partials<D>(base, p.n_splits, split, dc, M, num, den);
       xs[idx] = den > 0.0f ? num / den : 0.0f;
+    }
+    if (!last) return;
+    __syncthreads();  // every thread of the merger has read its words
+    for (int idx = tid; idx < GG * D; idx += kThreads) {
+      const int g = idx / D, dc = idx % D;
+      const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
+      clear_partials<D>(wsw + row * (size_t)p.n_splits * (D + kRecPad), p.n_splits, split, dc);
     }
   }
   lds_barrier();
