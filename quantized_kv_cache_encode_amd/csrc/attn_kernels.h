@@ -91,9 +91,9 @@ struct ScalarTable {
     for (int j = 0; j < LEVELS; ++j) m = fmaxf(m, fabsf(lv[j]));
     return m;
   }
-  // Table of head g, with the (transformed) query q' held in qs: every entry is the integer nearest to its value
-  // times 2^e_g (fix_exp), so the table of head g sums to at most 2^30 in magnitude along any choice of one
-  // entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
+  // Table of head g, with the (transformed) query q' times 2^e_g (fix_exp) held in qs: every entry is the
+  // integer nearest to its value times 2^e_g, so the table of head g sums to at most 2^30 in magnitude along
+  // any choice of one entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
   // column); each work item fills JPT consecutive columns of one (head group, row).
   template <int GG, int HW, int NT = kThreads>
   __device__ static void build(const AttnParams&, const float* qs, const float* qa, const float* lv, float* lut,
@@ -102,19 +102,16 @@ struct ScalarTable {
     constexpr int JPT = COLS < 4 ? COLS : 4;
     constexpr int NJ = COLS / JPT;
     constexpr int total = (GG / HW) * ROWS * NJ;
-    const float cmax = level_max(lv);
     E* L = reinterpret_cast<E*>(lut);
     for (int e = tid; e < total; e += NT) {
       const int j0 = (e % NJ) * JPT;
       const int r = (e / NJ) % ROWS;
       const int g0 = (e / (NJ * ROWS)) * HW;
-      float qv[HW][GRP];
+      float qv[HW][GRP];  // the rotated query elements, already times the head's scale 2^e_g
 #pragma unroll
-      for (int h = 0; h < HW; ++h) {
-        const float sc = pow2f(fix_exp(qa[g0 + h], cmax));
+      for (int h = 0; h < HW; ++h)
 #pragma unroll
-        for (int k = 0; k < GRP; ++k) qv[h][k] = qs[(g0 + h) * D + r * GRP + k] * sc;
-      }
+        for (int k = 0; k < GRP; ++k) qv[h][k] = qs[(g0 + h) * D + r * GRP + k];
       E* row = L + (size_t)(e / NJ) * COLS + j0;
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
@@ -246,11 +243,13 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
   return r;
 }
 
-// Loads the GG queries into qs[g][i] (fp32) and copies the codebook levels into LDS.  For the scalar codecs
-// (fixed-point tables) a query takes 8 consecutive coordinates per lane and d/8 lanes, and qa[g] receives
-// sum_i |q'_{g,i}|, the bound that sets the head's table scale.  For the Hadamard codec every query is also
-// rotated, q' = H D q / sqrt(d): sign flip, then a radix-2 fast Walsh-Hadamard transform (Sylvester order)
-// in registers (distances 1, 2, 4) and across the query's lanes (distances 8 .. d/2).
+// Loads the GG queries into qs[g][i] (fp32) and copies the codebook levels into LDS.  For the scalar codecs a
+// query takes 16 consecutive coordinates per lane and d/16 lanes (the write path's lane layout).  For the
+// Hadamard codec every query is rotated, q' = H D q / sqrt(d), with the write path's arithmetic: sign flip
+// folded into the first butterflies, in-register stages for coordinate distances 1 .. 8, lane swizzles for
+// 16 .. d/2 (Sylvester order, each stage a + b and a - b).  With fixed-point tables (qa != nullptr) qa[g]
+// receives sum_i |q'_{g,i}|, the bound that sets the head's table scale 2^e_g (fix_exp), and qs holds q'
+// already multiplied by 2^e_g, so the table build only multiplies by the levels and rounds.
 // `between` runs after this thread's query loads are issued and before they are used: the caller issues
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
@@ -258,73 +257,50 @@ template <class S, int GG, int NT = kThreads, class F>
 __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
   if (tid < 16) lv[tid] = p.levels[tid];
-  if constexpr (S::kIntLut) {
-    constexpr int LPQ = D / 8;  // lanes per query (a power of two <= 32, so groups never straddle waves)
-    static_assert(GG * LPQ <= NT, "one lane per 8 coordinates of every query");
+  if constexpr (S::kIntLut || S::kRotate) {
+    constexpr int LPQ = EncLanes<D>::LPK;  // lanes per query (a power of two <= 16, so groups never straddle waves)
+    static_assert(GG * LPQ <= NT, "one lane per 16 coordinates of every query");
     const int g = tid / LPQ, k = tid % LPQ;
-    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + 8 * k;
-    const uint32_t sb = (p.signs[(8 * k) >> 5] >> ((8 * k) & 31)) & 0xffu;
-    uint4 raw0 = make_uint4(0, 0, 0, 0), raw1 = make_uint4(0, 0, 0, 0);
+    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + kEncCpl * k;
+    uint32_t raw[kEncCpl];
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) raw[j] = 0u;
     if (g < GG) {
-      if (p.q_f16) {
-        raw0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off);
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + off);
-        raw0 = src[0];
-        raw1 = src[1];
+      const uint4* src = p.q_f16 ? reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off)
+                                 : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + off);
+      const int nv = p.q_f16 ? 2 : 4;  // 16-byte loads per lane
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        if (h < nv) {
+          const uint4 v = src[h];
+          raw[4 * h + 0] = v.x; raw[4 * h + 1] = v.y; raw[4 * h + 2] = v.z; raw[4 * h + 3] = v.w;
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     between();
     __builtin_amdgcn_sched_barrier(0);
-    if (g < GG) {
-      float x[8];
-      if (p.q_f16) {
-        const uint32_t r[4] = {raw0.x, raw0.y, raw0.z, raw0.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          x[2 * t] = h2f((uint16_t)(r[t] & 0xffffu));
-          x[2 * t + 1] = h2f((uint16_t)(r[t] >> 16));
-        }
-      } else {
-        const uint32_t r[8] = {raw0.x, raw0.y, raw0.z, raw0.w, raw1.x, raw1.y, raw1.z, raw1.w};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = __builtin_bit_cast(float, r[t]);
-      }
+    if (g < GG) {  // whole groups of LPQ lanes, so the swizzles stay within the query's lanes
+      float x[kEncCpl];
+      if (p.q_f16) key_lane_floats<true>(raw, x);
+      else key_lane_floats<false>(raw, x);
       if constexpr (S::kRotate) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if ((sb >> t) & 1u) x[t] = -x[t];
-#pragma unroll
-        for (int h = 1; h < 8; h <<= 1)
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            if ((t & h) == 0) {
-              const float a = x[t], b = x[t + h];
-              x[t] = a + b;
-              x[t + h] = a - b;
-            }
-#pragma unroll
-        for (int dl = 1; dl < LPQ; dl <<= 1) {
-          const bool upper = (k & dl) != 0;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float o = __shfl_xor(x[t], dl, 64);
-            x[t] = upper ? (o - x[t]) : (x[t] + o);
-          }
-        }
+        float sg[kEncCpl];
+        lane_signs<D>(p.signs, k, sg);
+        (void)rotate_key_lane<D>(x, k, sg);
       }
       const float rs = S::kRotate ? 1.0f / __builtin_sqrtf((float)D) : 1.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) qs[g * D + 8 * k + t] = x[t] * rs;
+      float sc = 1.0f;
       if (qa != nullptr) {  // sum_i |q'_i| of the query: the bound that scales its fixed-point table
         float a = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) a += fabsf(x[t]);
-#pragma unroll
-        for (int dl = 1; dl < LPQ; dl <<= 1) a += __shfl_xor(a, dl, 64);
-        if (k == 0) qa[g] = a * rs;
+        for (int j = 0; j < kEncCpl; ++j) a += fabsf(x[j]);
+        a = key_lanes_sum<LPQ>(a) * rs;
+        if (k == 0) qa[g] = a;
+        sc = pow2f(fix_exp(a, S::level_max(p.levels)));
       }
+#pragma unroll
+      for (int j = 0; j < kEncCpl; ++j) qs[g * D + kEncCpl * k + j] = (x[j] * rs) * sc;
     }
   } else {
     between();
