@@ -256,7 +256,12 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 template <class S, int GG, int NT = kThreads, class F>
 __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
   constexpr int D = S::D;
-  if (tid < 16) lv[tid] = p.levels[tid];
+  // the levels come from the kernel arguments with wave-uniform (scalar) reads: indexed per lane they would be
+  // a vector load from the argument segment whose wait would hold up everything issued after it
+  if (tid == 0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) lv[t] = p.levels[t];
+  }
   if constexpr (S::kIntLut || S::kRotate) {
     constexpr int LPQ = EncLanes<D>::LPK;  // lanes per query (a power of two <= 16, so groups never straddle waves)
     static_assert(GG * LPQ <= NT, "one lane per 16 coordinates of every query");
@@ -265,13 +270,18 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
     uint32_t raw[kEncCpl];
 #pragma unroll
     for (int j = 0; j < kEncCpl; ++j) raw[j] = 0u;
-    if (g < GG) {
-      const uint4* src = p.q_f16 ? reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off)
-                                 : reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + off);
-      const int nv = p.q_f16 ? 2 : 4;  // 16-byte loads per lane
+    if (g < GG) {  // 16 coordinates: two 16-byte loads (fp16) or four (fp32)
+      if (p.q_f16) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(p.q) + off);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        if (h < nv) {
+        for (int h = 0; h < 2; ++h) {
+          const uint4 v = src[h];
+          raw[4 * h + 0] = v.x; raw[4 * h + 1] = v.y; raw[4 * h + 2] = v.z; raw[4 * h + 3] = v.w;
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.q) + off);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
           const uint4 v = src[h];
           raw[4 * h + 0] = v.x; raw[4 * h + 1] = v.y; raw[4 * h + 2] = v.z; raw[4 * h + 3] = v.w;
         }

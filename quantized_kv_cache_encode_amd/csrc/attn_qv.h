@@ -585,7 +585,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
       }
     }
     const float rs = 1.0f / __builtin_sqrtf((float)D);
-    const uint32_t sb = (p.signs[(8 * kk) >> 5] >> ((8 * kk) & 31)) & 0xffu;
+    uint32_t sw = 0;  // the sign word of these coordinates, picked with uniform reads of the arguments
+#pragma unroll
+    for (int w = 0; w < (D + 31) / 32; ++w)
+      if (((8 * kk) >> 5) == w) sw = p.signs[w];
+    const uint32_t sb = (sw >> ((8 * kk) & 31)) & 0xffu;
     const size_t row = (size_t)u.b * p.Hq + u.h0 + g;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
