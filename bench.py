@@ -95,102 +95,147 @@ def algorithmic_bytes(shape, bpk, append=False):
     return n
 
 
+def oracle_threads():
+    """Host threads for the oracle: the cores this process may run on, at most 16 (one GPU's share of a box)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def time_oracle(tasks, min_seconds, threads):
+    """Wall time of passes over `tasks` (callables; the oracle's ctypes calls release the GIL, so a thread pool
+    runs them on `threads` cores), repeated until min_seconds have passed.  Returns (passes, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    passes, elapsed = 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while passes == 0 or elapsed < min_seconds:
+            t0 = time.perf_counter()
+            for _ in ex.map(lambda f: f(), tasks):
+                pass
+            elapsed += time.perf_counter() - t0
+            passes += 1
+    return passes, elapsed
+
+
+def oracle_record(tasks, units_per_pass, unit, min_seconds, what):
+    """The oracle timed on all of the host's cores (the reported figure) and on one thread (beside it)."""
+    threads = oracle_threads()
+    p1, s1 = time_oracle(tasks, min(3.0, min_seconds / 4), 1)
+    pn, sn = time_oracle(tasks, min_seconds, threads)
+    return {"value": pn * units_per_pass / sn, "unit": unit, "cores": threads, "kind": "oracle",
+            "value_1thread": p1 * units_per_pass / s1,
+            "sample": "%s: %d pass(es) in %.1f s on %d thread(s) (a thread pool over the tasks; %d pass(es) in "
+                      "%.1f s on one thread for value_1thread)" % (what, pn, sn, threads, p1, s1)}
+
+
 def cpu_baseline(shape, signs, q, min_seconds=5.0):
-    """Time the fp64 oracle (one thread) on the same decode step: all batches, repeated until min_seconds pass."""
+    """The fp64 oracle on the same decode step: for every (batch, kv head), the write path's encode of the new key
+    and decode attention of that kv head's query heads over all T cached keys."""
+    import numpy as np
+
     import oracle
     import workloads as W
 
     lv, th = oracle.codebook(shape.d, shape.b)
     scale = 1.0 / math.sqrt(shape.d)
-    cache = []
+    G = shape.Hq // shape.Hkv
+    newk = W.new_keys(shape).astype(np.float64)
+    q64 = q.astype(np.float64)
+    tasks = []
     for bi in range(shape.B):  # the prefilled cache: encoded by the oracle itself, untimed
         keys = W.keys(shape, batches=[bi])
         codes, norms, _, _ = oracle.encode_keys(th, signs, keys, shape.b)
-        cache.append((codes, norms, W.values(shape, batches=[bi])))
-    newk = W.new_keys(shape)
-    done_keys, elapsed, passes = 0, 0.0, 0
-    while elapsed < min_seconds or passes == 0:
-        t0 = time.perf_counter()
-        oracle.encode_keys(th, signs, newk, shape.b)                              # write path of the step
-        for bi, (codes, norms, v) in enumerate(cache):
-            oracle.decode_attn(lv, signs, q[bi:bi + 1], codes, norms, v, scale)  # read path of the step
-        elapsed += time.perf_counter() - t0
-        done_keys += shape.B * shape.Hq * shape.T
-        passes += 1
-    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": "the full decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode of the new "
-                      "keys + decode attention, one thread, %.1f s" % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+        v = W.values(shape, batches=[bi]).astype(np.float64)
+        for h in range(shape.Hkv):
+            args = (q64[bi:bi + 1, h * G:(h + 1) * G], codes[:, h:h + 1], norms[:, h:h + 1], v[:, h:h + 1],
+                    newk[bi:bi + 1, h:h + 1])
+
+            def task(a=args):
+                oracle.encode_keys(th, signs, a[4], shape.b)                       # write path of the step
+                oracle.decode_attn(lv, signs, a[0], a[1], a[2], a[3], scale)     # read path of the step
+            tasks.append(task)
+    return oracle_record(tasks, shape.B * shape.Hq * shape.T, "keys/s", min_seconds,
+                         "the full decode step (B=%d, Hq=%d, T=%d): fp64 C oracle encode of the new keys + decode "
+                         "attention, %d (batch, kv head) tasks" % (shape.B, shape.Hq, shape.T, len(tasks)))
 
 
 def cpu_baseline_qv(shape, signs, q, min_seconds=5.0):
-    """Time the fp64 oracle (one thread) on the quantized-value decode step, repeated until min_seconds pass."""
+    """The fp64 oracle on the quantized-value decode step, per (batch, kv head)."""
+    import numpy as np
+
     import oracle
     import workloads as W
 
     lv, th = oracle.codebook(shape.d, shape.b)
     scale = 1.0 / math.sqrt(shape.d)
-    cache = []
+    G = shape.Hq // shape.Hkv
+    q64 = q.astype(np.float64)
+    tasks = []
     for bi in range(shape.B):  # keys and values encoded by the oracle itself, untimed
         codes, norms, _, _ = oracle.encode_keys(th, signs, W.keys(shape, batches=[bi]), shape.b)
         vcodes, vnorms, _, _ = oracle.encode_keys(th, signs, W.values(shape, batches=[bi]), shape.b)
-        cache.append((codes, norms, vcodes, vnorms))
-    done_keys, elapsed, passes = 0, 0.0, 0
-    while elapsed < min_seconds or passes == 0:
-        t0 = time.perf_counter()
-        for bi, (codes, norms, vcodes, vnorms) in enumerate(cache):
-            oracle.decode_attn_qv(lv, signs, q[bi:bi + 1], codes, norms, vcodes, vnorms, scale)
-        elapsed += time.perf_counter() - t0
-        done_keys += shape.B * shape.Hq * shape.T
-        passes += 1
-    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": "the full quantized-value decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle "
-                      "(value dequantization + decode attention), one thread, %.1f s"
-                      % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+        for h in range(shape.Hkv):
+            args = (q64[bi:bi + 1, h * G:(h + 1) * G], codes[:, h:h + 1], norms[:, h:h + 1], vcodes[:, h:h + 1],
+                    vnorms[:, h:h + 1])
+
+            def task(a=args):
+                oracle.decode_attn_qv(lv, signs, a[0], a[1], a[2], a[3], a[4], scale)
+            tasks.append(task)
+    return oracle_record(tasks, shape.B * shape.Hq * shape.T, "keys/s", min_seconds,
+                         "the full quantized-value decode step (B=%d, Hq=%d, T=%d): fp64 C oracle (value "
+                         "dequantization + decode attention), %d (batch, kv head) tasks"
+                         % (shape.B, shape.Hq, shape.T, len(tasks)))
 
 
 def cpu_baseline_pot(shape, q, bits, mantissa, min_seconds=5.0):
-    """Time the fp64 oracle (one thread) on the power-of-two decode step, repeated until min_seconds pass."""
+    """The fp64 oracle on the power-of-two decode step, per (batch, kv head)."""
+    import numpy as np
+
     import oracle
     import workloads as W
 
     scale = 1.0 / math.sqrt(shape.d)
-    cache = []
+    G = shape.Hq // shape.Hkv
+    newk = W.new_keys(shape).astype(np.float64)
+    q64 = q.astype(np.float64)
+    tasks = []
     for bi in range(shape.B):  # the prefilled cache, encoded by the oracle itself, untimed
         codes, scales, _ = oracle.pot_encode(W.keys(shape, batches=[bi]), bits, mantissa)
-        cache.append((codes, scales, W.values(shape, batches=[bi])))
-    newk = W.new_keys(shape)
-    done_keys, elapsed, passes = 0, 0.0, 0
-    while elapsed < min_seconds or passes == 0:
-        t0 = time.perf_counter()
-        oracle.pot_encode(newk, bits, mantissa)                                      # write path of the step
-        for bi, (codes, scales, v) in enumerate(cache):
-            oracle.pot_decode_attn(q[bi:bi + 1], codes, scales, v, bits, mantissa, scale)  # read path
-        elapsed += time.perf_counter() - t0
-        done_keys += shape.B * shape.Hq * shape.T
-        passes += 1
-    return {"value": done_keys / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": "the full power-of-two decode step (B=%d, Hq=%d, T=%d) x %d pass(es): fp64 C oracle encode "
-                      "of the new keys + decode attention, one thread, %.1f s"
-                      % (shape.B, shape.Hq, shape.T, passes, elapsed)}
+        v = W.values(shape, batches=[bi]).astype(np.float64)
+        for h in range(shape.Hkv):
+            args = (q64[bi:bi + 1, h * G:(h + 1) * G], codes[:, h:h + 1], scales[:, h:h + 1], v[:, h:h + 1],
+                    newk[bi:bi + 1, h:h + 1])
+
+            def task(a=args):
+                oracle.pot_encode(a[4], bits, mantissa)                                  # write path
+                oracle.pot_decode_attn(a[0], a[1], a[2], a[3], bits, mantissa, scale)    # read path
+            tasks.append(task)
+    return oracle_record(tasks, shape.B * shape.Hq * shape.T, "keys/s", min_seconds,
+                         "the full power-of-two decode step (B=%d, Hq=%d, T=%d): fp64 C oracle encode of the new "
+                         "keys + decode attention, %d (batch, kv head) tasks" % (shape.B, shape.Hq, shape.T, len(tasks)))
 
 
 def cpu_baseline_encode(shape, signs, min_seconds=5.0):
-    """Time the fp64 oracle's encode (one thread) on batch 0 of the workload, repeated until min_seconds pass."""
+    """The fp64 oracle's encode on batch 0 of the workload, per kv head."""
     import oracle
     import workloads as W
 
     _, th = oracle.codebook(shape.d, shape.b)
     keys = W.keys(shape, batches=[0])
-    done, elapsed, passes = 0, 0.0, 0
-    while elapsed < min_seconds or passes == 0:
-        t0 = time.perf_counter()
-        oracle.encode_keys(th, signs, keys, shape.b)
-        elapsed += time.perf_counter() - t0
-        done += keys.shape[0] * keys.shape[1] * keys.shape[2]
-        passes += 1
-    return {"value": done / elapsed, "unit": "keys/s", "cores": 1, "kind": "oracle",
-            "sample": "batch 0 of the workload (Hkv=%d x T=%d keys, d=%d) x %d pass(es): fp64 C oracle encode, one "
-                      "thread, %.1f s" % (shape.Hkv, shape.T, shape.d, passes, elapsed)}
+    tasks = []
+    for h in range(shape.Hkv):
+        kh = keys[:, h:h + 1].copy()
+
+        def task(k=kh):
+            oracle.encode_keys(th, signs, k, shape.b)
+        tasks.append(task)
+    n = keys.shape[0] * keys.shape[1] * keys.shape[2]
+    return oracle_record(tasks, n, "keys/s", min_seconds,
+                         "batch 0 of the workload (Hkv=%d x T=%d keys, d=%d): fp64 C oracle encode, %d kv-head tasks"
+                         % (shape.Hkv, shape.T, shape.d, len(tasks)))
 
 
 def run_encode(K, torch, a):
@@ -258,7 +303,7 @@ def run_encode(K, torch, a):
         "metric": "cached keys encoded/sec and % of HBM roofline, Hadamard/Lloyd-Max write path, B=64 T=8k",
         "value": value, "unit": "keys/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": "f32 (norm, rotation, code search on fp16 keys)", "data": "synthetic",
         "config": {"workload": "sweep encode: B=64 Hkv=8 d=128 b=4 T=8192, fp16 keys", "B": B, "Hkv": Hkv, "d": d,
                    "b": b, "T": T, "k_dtype": "f16",
                    "step": "one kvq_encode_keys call: norm, rotation, codes and norms of B*Hkv*T keys",
@@ -269,6 +314,74 @@ def run_encode(K, torch, a):
                                "code search + packing)",
                      "avg_launch_ms": ms_per_step, "algorithmic_bytes": alg_bytes},
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def run_stream(K, torch, a):
+    """The streaming ceiling of the long-context decode step: kvq_stream_read reads the same codes, norms and fp16
+    V (171,966,464 bytes) with the decode kernel's grid, split and access pattern and does nothing else; four
+    copies of the cache rotate, as in the decode step's timing."""
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    shape = W.LONGCTX
+    B, Hq, Hkv, d, T, b = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T, shape.b
+    bpk = d * b // 8
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    caches = []
+    for _ in range(a.caches):  # contents do not matter to a plain read; random bytes of the right sizes
+        caches.append((torch.randint(0, 256, (B, Hkv, T, bpk), dtype=torch.uint8, device=dev, generator=g),
+                       torch.rand((B, Hkv, T), device=dev, generator=g),
+                       torch.randn((B, Hkv, T, d), device=dev, generator=g).half()))
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    cb = K.kvq_build_codebook(d, b)
+    ws = K.kvq_decode_attn_workspace(cb, B, Hq, Hkv, T, a.splits)
+    splits = ws // (B * Hq * (d + 4) * 4) if ws else 1  # the decode step's split count
+
+    def step(i):
+        c, n, v = caches[i % len(caches)]
+        K.kvq_stream_read(c, n, v, splits, sink)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(max(a.warmup, len(caches))):
+            step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for i in range(a.steps):
+            step(i)
+    settle(torch, gr.replay, a.settle_seconds)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    gr.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    nbytes = B * Hkv * T * (bpk + 4 + 2 * d)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    eprint("plain read %.4f ms: %d bytes -> %.1f GB/s = %.1f%% of %.0f GB/s" % (ms, nbytes, gbs,
+                                                                             100 * gbs / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    rec = {
+        "metric": "streaming ceiling: plain read of the long-context decode cache with the decode access pattern, "
+                  "GB/s and % of HBM roofline",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32 (checksum only)",
+        "data": "synthetic",
+        "config": {"workload": "longctx cache: B=8 Hkv=4 d=64 b=4 T=32768, codes + fp32 norms + fp16 V",
+                   "B": B, "Hkv": Hkv, "d": d, "b": b, "T": T, "t_splits": int(splits),
+                   "caches_rotated": len(caches),
+                   "step": "one kvq_stream_read launch: 12-wave workgroups, 64 tokens per wave and chunk, one chunk "
+                           "ahead, non-temporal loads"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "stream_read_kernel",
+                     "avg_launch_ms": ms, "algorithmic_bytes": nbytes},
+        "cpu_baseline": None,
     }
     print(json.dumps(rec), flush=True)
     return 0
@@ -518,11 +631,13 @@ def main(argv=None):
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline step, time every workload and operation (table on stderr)")
-    ap.add_argument("--variant", choices=("append", "qv", "pot", "encode"), default="append",
+    ap.add_argument("--variant", choices=("append", "qv", "pot", "encode", "stream"), default="append",
                     help="append: the fused append + decode step over fp16 V (default); qv: decode attention "
                          "with the values stored as codes of the same codec (kvq_decode_attn_qv); pot: the fused "
                          "step with 4-bit power-of-two key codes (with the mantissa term) instead; encode: the "
-                         "write path alone at the batch-64 sweep shape (kvq_encode_keys)")
+                         "write path alone at the batch-64 sweep shape (kvq_encode_keys); stream: a plain read "
+                         "of the long-context cache with the decode kernel's grid and access pattern "
+                         "(kvq_stream_read), the streaming ceiling the decode step is measured against")
     a = ap.parse_args(argv)
 
     if a.gpus != 1:
@@ -546,6 +661,8 @@ def main(argv=None):
         return 0
     if a.variant == "encode":
         return run_encode(K, torch, a)
+    if a.variant == "stream":
+        return run_stream(K, torch, a)
     dev = torch.device("cuda:0")
     shape = W.LONGCTX
     B, Hq, Hkv, d, T, b = shape.B, shape.Hq, shape.Hkv, shape.d, shape.T, shape.b
@@ -667,7 +784,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "int32 fixed-point LUT sums; fp16 P x fp16 V on MFMA with fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": "longctx decode: B=8 Hq=32 Hkv=4 d=64 b=4 T=32768, fp16 q/k/v",
                    "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "b": b, "T": T, "v_dtype": "f16",

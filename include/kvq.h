@@ -319,6 +319,25 @@ kvq_status kvq_select_signs(const kvq_codebook* cb, const int8_t* candidates, in
                             int n_cal, int Hq, int Hkv, int64_t T, float scale, float* errors, int* best,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/* Measurement aid, not a step of the method: the streaming ceiling of
+ * kvq_decode_attn on this cache.  Reads every byte a decode call reads from
+ * the cache -- codes, norms and fp16 V of every (batch, kv head) row below
+ * T_cap -- with the decode kernel's grid (the token axis cut into n_splits
+ * spans of a multiple of 64 tokens, one workgroup of 12 waves per span and
+ * (batch, kv head)) and access pattern (64 tokens per wave and chunk, one
+ * chunk requested ahead, non-temporal loads), and discards it.
+ *   codes: device [B][Hkv][T_cap][bytes_per_key]; norms: device
+ *     [B][Hkv][T_cap] fp32; v: device [B][Hkv][T_cap][d] fp16; all 16-byte
+ *     aligned.  Built for d = 64 with 32-byte code rows and d = 128 with
+ *     64-byte code rows.
+ *   n_splits: 1..256 (the split kvq_decode_attn_workspace's n_splits picks).
+ *   sink: device, >= 4 bytes; written only when a checksum of the data hits a
+ *     fixed value (so the loads cannot be elided).
+ * Errors: KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED (other d or row size, or
+ *   T_cap * 4 * max(d, 32) >= 2^31), KVQ_ERR_DEVICE. */
+kvq_status kvq_stream_read(const uint8_t* codes, const float* norms, const void* v, int B, int Hkv, int64_t T_cap,
+                           int d, int bytes_per_key, int n_splits, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

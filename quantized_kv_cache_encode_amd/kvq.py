@@ -81,6 +81,7 @@ _lib.kvq_decode_attn_append.argtypes = [_CB, _P, _P, _i32, _P, _i32, _P, _P, _P,
                                         _f32, _P, _i32, _P, _sz, _i32, _P]
 _lib.kvq_decode_attn_noalloc.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _i32, _i32, _i32, _i32, _i64, _P, _f32,
                                          _P, _i32, _i32, _P]
+_lib.kvq_stream_read.argtypes = [_P, _P, _P, _i32, _i32, _i64, _i32, _i32, _i32, _P, _P]
 _lib.kvq_decode_attn_qv.argtypes = [_CB, _P, _P, _i32, _P, _P, _P, _P, _i32, _i32, _i32, _i64, _P, _f32, _P, _i32,
                                     _P, _sz, _i32, _P]
 _lib.kvq_select_signs_workspace.argtypes = [_CB, _i32, _i32, _i32, _i64, _i32]
@@ -89,13 +90,13 @@ _lib.kvq_select_signs.argtypes = [_CB, _P, _i32, _P, _i32, _P, _i32, _P, _i32, _
                                   _P, _sz, _P]
 for _f in ("kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq", "kvq_encode_keys", "kvq_score",
            "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_append", "kvq_decode_attn_qv",
-           "kvq_select_signs"):
+           "kvq_select_signs", "kvq_stream_read"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 EXPORTS = ("kvq_version", "kvq_last_error", "kvq_build_codebook", "kvq_build_codebook_pot", "kvq_build_codebook_pq", "kvq_codebook_pq",
            "kvq_encode_keys", "kvq_score", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_noalloc",
            "kvq_decode_attn_append",
-           "kvq_decode_attn_qv", "kvq_select_signs_workspace", "kvq_select_signs")
+           "kvq_decode_attn_qv", "kvq_select_signs_workspace", "kvq_select_signs", "kvq_stream_read")
 
 
 def _check(status: int):
@@ -308,6 +309,17 @@ def kvq_decode_attn_append(cb: kvq_codebook, signs, new_keys: torch.Tensor, q: t
                                        _dev(seq_lens, "seq_lens", torch.int32, optional=True), float(scale),
                                        _dev(out, "out"), _dt(out), ws_ptr, ws_bytes, n_splits, _stream(stream)))
     return out
+
+
+def kvq_stream_read(codes: torch.Tensor, norms: torch.Tensor, v: torch.Tensor, n_splits: int, sink: torch.Tensor,
+                    stream=None):
+    """Plain read of a decode cache (codes [B][Hkv][T_cap][bpk], norms, fp16 v [B][Hkv][T_cap][d]) with the decode
+    kernel's access pattern: the streaming ceiling of kvq_decode_attn on it."""
+    B, Hkv, T_cap, bpk = codes.shape
+    d = v.shape[-1]
+    _check(_lib.kvq_stream_read(_dev(codes, "codes", torch.uint8), _dev(norms, "norms", torch.float32),
+                                _dev(v, "v", torch.float16), B, Hkv, T_cap, d, bpk, n_splits, _dev(sink, "sink"),
+                                _stream(stream)))
 
 
 def kvq_select_signs_workspace(cb: kvq_codebook, n_cal: int, Hq: int, Hkv: int, T: int, C: int) -> int:

@@ -24,7 +24,8 @@ def K():
 
 
 def test_exports_every_declared_symbol(K):
-    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    import glob
+    hdr = "".join(open(h).read() for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))))
     declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kvq_[a-z_0-9]+)\s*\(", hdr, flags=re.M))
     assert declared >= {"kvq_build_codebook", "kvq_encode_keys", "kvq_score", "kvq_decode_attn"}
     lib = ctypes.CDLL(K.LIB_PATH)
