@@ -20,13 +20,17 @@
 
 namespace kvq {
 
-template <int D, int BITS, bool KF16>
-__global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
+// WHOLE: the new keys fill whole cache rows (p.rows_whole), so key i of the launch goes to row i.
+template <int D, int BITS, bool KF16, bool WHOLE>
+// amdgpu_waves_per_eu(5): at most 96 registers, five waves per SIMD (the kernel needs no more; with 97 the
+// compiler's own choice left four per SIMD, measured 4 % slower).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void hlm_encode_kernel(const EncodeParams p) {
   constexpr int LPK = EncLanes<D>::LPK;  // lanes per key
   constexpr int BPK = D * BITS / 8;    // code bytes per key
   constexpr int L = 1 << BITS;
   constexpr int ESZ = KF16 ? 2 : 4;
-  __shared__ float2 cells[kEncodeMaxCells];  // (threshold inside the cell or +inf, count below the cell)
+  // per cell, 16 bytes apart: the threshold inside the cell (or +inf) and the count of thresholds below it
+  __shared__ float4 cells[kEncodeMaxCells];
 
   // cell table: the count of thresholds in lower cells and the one threshold (if any) inside the cell
   for (int c = threadIdx.x; c < p.n_cells; c += 256) {
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
       below += cj < c ? 1 : 0;
       if (cj == c) inside = p.thresholds[j];
     }
-    cells[c] = make_float2(inside, __builtin_bit_cast(float, below));
+    cells[c] = make_float4(inside, __builtin_bit_cast(float, below), 0.0f, 0.0f);
   }
   __syncthreads();
 
@@ -46,11 +50,18 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
   const int lk = tid & (LPK - 1);
   float sg[kEncCpl];
   lane_signs<D>(p.signs, lk, sg);
+  // The cell's byte offset in the table comes straight from the bits of v = y * cell_inv + cell_shift + 2^19.
+  // In [2^19, 2^20) the spacing of floats is 1/16, so the mantissa holds 16 v rounded to the nearest
+  // sixteenth, and masking off its low four bits leaves 16 * cell.  The rounding moves v by at most 1/32 of
+  // a cell, and every threshold sits at least 5% of a cell inside its cell (choose_encode_cells), so where it
+  // moves v into the neighbouring cell no threshold lies in between and the count is the same.  The shift
+  // is a multiple of 1/16 below 2^18, so adding 2^19 to it is exact.  y is finite with |y| <= 1 up to
+  // rounding (keys with a non-finite coordinate do not get here), and the cells span |y| <= 1.0001 with a
+  // spare cell at either end, so v is positive and the cell is in range without a clamp.
+  const float shift19 = p.cell_shift + 0x1p19f;
   auto code_of = [&](float y) -> uint32_t {
-    // y is finite with |y| <= 1 up to rounding (keys with a non-finite coordinate do not get here), and the cells span
-    // |y| <= 1.0001 with a spare cell at either end, so the cell index is in range without a clamp
-    const int c = (int)__builtin_fmaf(y, p.cell_inv, p.cell_shift);
-    const float2 e = cells[c];
+    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(y, p.cell_inv, shift19)) & 0x7ffff0u;
+    const float2 e = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(cells) + off);
     return (uint32_t)__builtin_bit_cast(int, e.y) + (y >= e.x ? 1u : 0u);
   };
   const int64_t n_keys = p.key_end - p.key_begin;
@@ -60,6 +71,11 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
   walk_keys<D, KF16>(keys, kb, ke, tid, [&](int64_t k, uint32_t (&raw)[kEncCpl], auto&& refill) {
     float x[kEncCpl];
     key_lane_floats<KF16>(raw, x);
+    // the coordinates are converted here, so that raw is free and the loads two passes ahead go out now (left
+    // alone, the compiler reads raw's fp16 halves in later mixed-precision FMAs, and the later refill measured
+    // slower)
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) asm volatile("" : "+v"(x[j]));
     refill();
     const float ss = rotate_key_lane<D>(x, lk, sg);
     float nrm;
@@ -81,7 +97,8 @@ __global__ __launch_bounds__(256) void hlm_encode_kernel(const EncodeParams p) {
       packed = encode_beyond_range<D, BITS>(x, lk, sg, ss, nrm, code_of);
     }
 
-    const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
+    if (k >= ke) return;  // past the workgroup's keys (the last pair of passes)
+    const int64_t row = WHOLE ? p.key_begin + k : encode_row(p, (uint32_t)(p.key_begin + k));
     if (row < 0) return;
     store_code_bits<BITS, true>(p.codes + row * BPK, lk, packed);
     if (lk == 0) p.norms[row] = nrm;
@@ -101,8 +118,13 @@ static hipError_t encode_launch(bool kf16, const EncodeParams& p0, hipStream_t s
     p.key_end = k0 + per_launch < n_keys ? k0 + per_launch : n_keys;
     p.keys_per_block = encode_keys_per_block(p.key_end - p.key_begin, KPB);
     const dim3 grid((unsigned)((p.key_end - p.key_begin + p.keys_per_block - 1) / p.keys_per_block));
-    if (kf16) hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, false>), grid, dim3(256), 0, s, p);
+    if (p.rows_whole) {
+      if (kf16) hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, true, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, false, true>), grid, dim3(256), 0, s, p);
+    } else {
+      if (kf16) hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, true, false>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((hlm_encode_kernel<D, BITS, false, false>), grid, dim3(256), 0, s, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

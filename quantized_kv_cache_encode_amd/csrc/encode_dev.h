@@ -293,8 +293,9 @@ __device__ __forceinline__ uint64_t pot_encode_lane(const float (&x)[kEncCpl], c
 // register sets, so two fetches stay in flight while a pass computes; a fetch past `end` reads zeros.
 // step(k, raw, refill) gets the key index k and the lane's coordinates as raw bits (packed fp16 halves in
 // raw[0..7], or fp32), and calls refill() once it no longer needs raw (which then starts the fetch two
-// passes ahead into it).  Every lane of a key takes the same trip count, so cross-lane steps see all of
-// them.
+// passes ahead into it).  In the last pair of passes some keys may be at or past `end` (their coordinates
+// read as zeros): step must store nothing for k >= end.  Every lane of a key takes the same trip count, so
+// cross-lane steps see all of them.
 template <int D, bool KF16, class Step>
 __device__ __forceinline__ void walk_keys(const void* keys, int64_t begin, int64_t end, int tid, Step&& step) {
   constexpr int LPK = EncLanes<D>::LPK;
@@ -305,23 +306,29 @@ __device__ __forceinline__ void walk_keys(const void* keys, int64_t begin, int64
   const int n = (int)(end - begin);  // the host keeps n * D * ESZ below 2^31
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(reinterpret_cast<const char*>(keys) + begin * D * ESZ), 0, n * D * ESZ, 0x00020000);
-  auto fetch = [&](int rel, uint32_t (&r)[kEncCpl]) {
+  // The two register sets are kept as 16-byte vectors, the loads' own type, and the passes come in pairs
+  // with no exit between them, so that each refill lands in the registers the next pass reads: as 32-bit
+  // words, or with an exit between the passes, the compiler swapped the sets through register copies at
+  // the loop's back edge, and a copy has to wait for every load in flight.
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  auto fetch = [&](int rel, u4 (&r)[NV]) {
     const int off = rel * D * ESZ + lk * kEncCpl * ESZ;
 #pragma unroll
-    for (int h = 0; h < NV; ++h) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16 * h, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) r[4 * h + j] = v[j];
-    }
+    for (int h = 0; h < NV; ++h) r[h] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + 16 * h, 0, 0);
   };
-  uint32_t ra[kEncCpl], rb[kEncCpl];
+  u4 ra[NV], rb[NV];
   int rel = tid / LPK;
   fetch(rel, ra);
+  __builtin_amdgcn_sched_barrier(0);  // ra's loads first: the loop's waits count on that order
   fetch(rel + KPB, rb);
-  auto pass = [&](int r, uint32_t (&buf)[kEncCpl]) { step(begin + r, buf, [&] { fetch(r + 2 * KPB, buf); }); };
+  auto pass = [&](int r, u4 (&buf)[NV]) {
+    uint32_t raw[kEncCpl];
+#pragma unroll
+    for (int j = 0; j < kEncCpl; ++j) raw[j] = j < 4 * NV ? buf[j / 4 < NV ? j / 4 : 0][j % 4] : 0u;
+    step(begin + r, raw, [&] { fetch(r + 2 * KPB, buf); });
+  };
   for (; rel < n; rel += 2 * KPB) {
     pass(rel, ra);
-    if (rel + KPB >= n) break;
     pass(rel + KPB, rb);
   }
 }

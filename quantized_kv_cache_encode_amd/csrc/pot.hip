@@ -32,6 +32,7 @@ __global__ __launch_bounds__(256) void pot_encode_kernel(const EncodeParams p) {
     refill();
     float alpha;
     const uint64_t packed = pot_encode_lane<D, BITS, MANT>(x, p.thresholds, alpha);
+    if (k >= ke) return;  // past the workgroup's keys (the last pair of passes)
     const int64_t row = encode_row(p, (uint32_t)(p.key_begin + k));
     if (row < 0) return;
     store_code_bits<BITS, true>(p.codes + row * BPK, lk, packed);
