@@ -21,6 +21,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -82,6 +83,50 @@ def settle(torch, replay, seconds, min_replays=3, max_replays=2000):
         torch.cuda.synchronize()
         n += 1
     return n
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of known size (256 MiB read + 256 MiB written per launch, three launches):
+    the kernel whose FETCH_SIZE / WRITE_SIZE readings scale the counters of the library's kernels."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def pmc_summary(path, kernel_regex):
+    """Per-dispatch means of the counters in a rocprofv3 --pmc CSV (a file, or a directory searched for
+    *counter_collection.csv), for the dispatches whose kernel name matches kernel_regex, grouped by kernel
+    and grid size; the plain copy kernel is listed too, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import csv
+    import glob
+
+    files = [path] if os.path.isfile(path) else sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"),
+                                                                recursive=True))
+    if not files:
+        print("no *counter_collection.csv under %s" % path)
+        return 1
+    pat = re.compile(kernel_regex)
+    groups = {}  # (short name, grid) -> counter -> [values]
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if not (pat.search(name) or "copyBuffer" in name):
+                    continue
+                short = name.split("(")[0].replace("void ", "")[:90]
+                key = (short, r.get("Grid_Size", "?"), r.get("Workgroup_Size", "?"))
+                d = groups.setdefault(key, {})
+                d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    for (short, grid, wg), counters in sorted(groups.items()):
+        n = max(len(v) for v in counters.values())
+        print("%s  grid=%s wg=%s  dispatches=%d" % (short, grid, wg, n))
+        for cn in sorted(counters):
+            v = counters[cn]
+            print("  %-28s mean %14.1f  min %14.1f  max %14.1f" % (cn, sum(v) / len(v), min(v), max(v)))
+    return 0
 
 
 def algorithmic_bytes(shape, bpk, append=False):
@@ -282,12 +327,7 @@ def run_encode(K, torch, a):
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_stop) / a.steps
     if a.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
     n_keys = B * Hkv * T
     value = n_keys / (ms_per_step * 1e-3)
     alg_bytes = n_keys * (2 * d + bpk + 4)
@@ -387,7 +427,7 @@ def run_stream(K, torch, a):
     return 0
 
 
-def run_suite(K, torch, reps=5, calls=30):
+def run_suite(K, torch, reps=5, calls=30, only=None, settle_seconds=0.3):
     """Every configuration of the method on one GPU: read path (fused decode, scores alone), write path
     (encode), and the PQ variant.  Inputs are drawn on the GPU from a seeded generator with the workloads'
     shapes and distributions (normal keys and values; per-(kv head, channel) LogNormal(0,1) scales for the
@@ -430,9 +470,9 @@ def run_suite(K, torch, reps=5, calls=30):
         with torch.cuda.graph(g):
             for i in range(calls):
                 fn(i)
-        for _ in range(3):  # the first replays of a new graph run slower
-            g.replay()
-        torch.cuda.synchronize()
+        # untimed replays until the clocks have settled under this load (a few replays alone left the short
+        # kernels 1-5 us per call slower than their steady state)
+        settle(torch, g.replay, settle_seconds)
         ts = []
         for _ in range(reps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -444,6 +484,19 @@ def run_suite(K, torch, reps=5, calls=30):
         ts.sort()
         return ts[len(ts) // 2] * 1e-3  # seconds per call
 
+    ops = ("decode", "append+dec", "score", "encode", "decode-qv", "pot-decode", "pot-encode", "pot-m-decode",
+           "pot-m-encode", "select/cand")
+
+    def want(name, op=None):
+        """--only: a regular expression searched in "<workload> <operation>"; rows that do not match are skipped."""
+        if only is None:
+            return True
+        return any(re.search(only, name + " " + o) for o in ((op,) if op else ops))
+
+    def measure(name, op, fn, n_rot, nbytes, keys_scored, cached):
+        if want(name, op):
+            row(name, op, timed(fn, n_rot), nbytes, keys_scored, cached)
+
     def row(name, op, sec, nbytes, keys_scored, cached):
         rows.append((name, op, sec * 1e6, nbytes / sec / 1e9, 100 * nbytes / sec / 1e9 / HBM_PEAK_GBS,
                      keys_scored / sec if keys_scored else 0.0, cached / sec))
@@ -451,6 +504,8 @@ def run_suite(K, torch, reps=5, calls=30):
 
     hlm = [("llama8b", W.LLAMA8B), ("longctx", W.LONGCTX)] + [(s.name, s) for s in W.SWEEP]
     for name, sh in hlm:
+        if not want(name):
+            continue
         B, Hq, Hkv, d, T, b = sh.B, sh.Hq, sh.Hkv, sh.d, sh.T, sh.b
         cb = K.kvq_build_codebook(d, b)
         bpk = cb.bytes_per_key
@@ -489,10 +544,11 @@ def run_suite(K, torch, reps=5, calls=30):
             K.kvq_score(cb, signs, q, c, n, scores=scores)
 
         rd = algorithmic_bytes(sh, bpk)
-        timed(dec, n_rot)  # untimed: the first graph of a workload runs slower (clocks, page tables)
-        row(name, "decode", timed(dec, n_rot), rd, B * Hq * T, B * Hkv * T)
-        row(name, "append+dec", timed(app, n_rot), algorithmic_bytes(sh, bpk, append=True), B * Hq * T, B * Hkv * T)
-        row(name, "score", timed(score, n_rot), B * Hkv * T * (bpk + 4) + B * Hq * T * 4, B * Hq * T, B * Hkv * T)
+        if want(name, "decode"):
+            timed(dec, n_rot)  # untimed: the first graph of a workload runs slower (clocks, page tables)
+        measure(name, "decode", dec, n_rot, rd, B * Hq * T, B * Hkv * T)
+        measure(name, "append+dec", app, n_rot, algorithmic_bytes(sh, bpk, append=True), B * Hq * T, B * Hkv * T)
+        measure(name, "score", score, n_rot, B * Hkv * T * (bpk + 4) + B * Hq * T * 4, B * Hq * T, B * Hkv * T)
 
         # the encode reads its keys from n_rot copies too, so that they stream from HBM rather than the
         # last-level cache
@@ -502,7 +558,7 @@ def run_suite(K, torch, reps=5, calls=30):
             c, n, _ = caches[i % n_rot]
             K.kvq_encode_keys(cb, signs, key_srcs[i % n_rot], c, n)
 
-        row(name, "encode", timed(enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
+        measure(name, "encode", enc, n_rot, B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
 
         # values stored with the same codec (rotated-domain AV, one inverse transform per head)
         vcs = []
@@ -520,7 +576,7 @@ def run_suite(K, torch, reps=5, calls=30):
             vc, vn = vcs[i % n_rot]
             K.kvq_decode_attn_qv(cb, signs, q, c, n, vc, vn, out=out, workspace=ws)
 
-        row(name, "decode-qv", timed(dec_qv, n_rot), B * Hkv * T * 2 * (bpk + 4) + B * Hq * d * 2, B * Hq * T,
+        measure(name, "decode-qv", dec_qv, n_rot, B * Hkv * T * 2 * (bpk + 4) + B * Hq * d * 2, B * Hq * T,
             B * Hkv * T)
         del vcs
 
@@ -546,8 +602,8 @@ def run_suite(K, torch, reps=5, calls=30):
                 K.kvq_encode_keys(pcb, None, key_srcs[i % n_rot], c, n)
 
             tag = "pot-m" if mant else "pot"
-            row(name, tag + "-decode", timed(pot_dec, n_rot), rd, B * Hq * T, B * Hkv * T)
-            row(name, tag + "-encode", timed(pot_enc, n_rot), B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
+            measure(name, tag + "-decode", pot_dec, n_rot, rd, B * Hq * T, B * Hkv * T)
+            measure(name, tag + "-encode", pot_enc, n_rot, B * Hkv * T * (2 * d + bpk + 4), 0, B * Hkv * T)
             del pcs
         del caches, keys, key_srcs, scores
         torch.cuda.empty_cache()
@@ -555,6 +611,8 @@ def run_suite(K, torch, reps=5, calls=30):
     # product quantization (LOOKAT-style ADC) at the GPT-2-small-like shapes: byte codes (K = 256) and
     # 4-bit codes (K = 16, two subspaces per byte) at 32x and 64x compression
     for sh in (W.PQ_GPT2, W.PQ4_GPT2_32X, W.PQ4_GPT2_64X):
+        if not want(sh.name):
+            continue
         B, H, d, T, m, Kc = sh.B, sh.Hq, sh.d, sh.T, sh.m, sh.K
         cent = rnd(H, m, Kc, d // m)
         cb = K.kvq_codebook_pq(d, m, Kc, H, cent)
@@ -583,11 +641,13 @@ def run_suite(K, torch, reps=5, calls=30):
             K.kvq_encode_keys(cb, None, keys, c)
 
         nkeys = B * H * T
-        row(sh.name, "decode", timed(pq_dec, n_rot), nkeys * (bpk + 2 * d) + B * H * d * 2, nkeys, nkeys)
-        row(sh.name, "score", timed(pq_score, n_rot), nkeys * (bpk + 4), nkeys, nkeys)
-        row(sh.name, "encode", timed(pq_enc, n_rot), nkeys * (2 * d + bpk), 0, nkeys)
+        measure(sh.name, "decode", pq_dec, n_rot, nkeys * (bpk + 2 * d) + B * H * d * 2, nkeys, nkeys)
+        measure(sh.name, "score", pq_score, n_rot, nkeys * (bpk + 4), nkeys, nkeys)
+        measure(sh.name, "encode", pq_enc, n_rot, nkeys * (2 * d + bpk), 0, nkeys)
         del caches, keys, vals
     torch.cuda.empty_cache()
+    if not want("signsel_200"):
+        return rows
 
     # one-time sign-pattern selection: 200 candidates on 8 calibration samples of 512 keys.  The call is
     # synchronous (it returns the ranking to the host), so it is timed by wall clock, not in a graph; the
@@ -631,6 +691,9 @@ def main(argv=None):
                     help="also run one 256 MiB device copy (a known-size kernel for scaling HBM counters)")
     ap.add_argument("--suite", action="store_true",
                     help="instead of the headline step, time every workload and operation (table on stderr)")
+    ap.add_argument("--only", default=None, metavar="REGEX",
+                    help="with --suite: time only the rows whose \"<workload> <operation>\" matches REGEX "
+                         "(e.g. 'longctx score')")
     ap.add_argument("--variant", choices=("append", "qv", "pot", "encode", "stream"), default="append",
                     help="append: the fused append + decode step over fp16 V (default); qv: decode attention "
                          "with the values stored as codes of the same codec (kvq_decode_attn_qv); pot: the fused "
@@ -638,8 +701,14 @@ def main(argv=None):
                          "write path alone at the batch-64 sweep shape (kvq_encode_keys); stream: a plain read "
                          "of the long-context cache with the decode kernel's grid and access pattern "
                          "(kvq_stream_read), the streaming ceiling the decode step is measured against")
+    ap.add_argument("--pmc-summary", default=None, metavar="PATH",
+                    help="no benchmark: print per-dispatch counter means from a rocprofv3 --pmc CSV output "
+                         "(file or directory) for the kernels matching --kernel")
+    ap.add_argument("--kernel", default=".", metavar="REGEX", help="with --pmc-summary: kernel-name filter")
     a = ap.parse_args(argv)
 
+    if a.pmc_summary:
+        return pmc_summary(a.pmc_summary, a.kernel)
     if a.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (got --gpus %d)" % a.gpus)
         return 2
@@ -657,7 +726,9 @@ def main(argv=None):
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if a.suite:
-        run_suite(K, torch)
+        run_suite(K, torch, only=a.only)
+        if a.calibrate_copy:
+            copy_calibration(torch)
         return 0
     if a.variant == "encode":
         return run_encode(K, torch, a)
@@ -746,13 +817,7 @@ def main(argv=None):
     attn_avg_ms = ms_per_step
 
     if a.calibrate_copy:
-        # a plain device-to-device copy of known size: 256 MiB read + 256 MiB written per launch
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch)
 
     key_scores = B * Hq * T
     value = key_scores / (ms_per_step * 1e-3)

@@ -125,20 +125,20 @@ int device_cus() {
 }
 
 // Split of the token axis: every split is a multiple of 64 tokens.  With no
-// request, aim for one workgroup per compute unit (one round of the grid) but
+// request, aim for per_cu workgroups per compute unit (one round of the grid) but
 // keep at least one 64-token chunk per wave in a split.  A launch that would
 // then fill less than half the compute units with two or more splits per unit
 // is all latency: there a split may hold half that, which halves each
 // workgroup's serial part, up to about half the compute units (beyond that,
 // and from one split to two, the merge costs more than the shorter splits
 // save).
-void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len) {
+void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len, int per_cu = 1) {
   const int64_t max_splits = (T_cap + 63) / 64;
   int64_t s;
   if (requested > 0) {
     s = requested < max_splits ? requested : max_splits;
   } else {
-    const int64_t target = (int64_t)device_cus();
+    const int64_t target = (int64_t)device_cus() * per_cu;
     s = (target + units - 1) / units;
     const int64_t min_tokens = kvq::kReadThreads;  // 64 tokens for each of the workgroup's waves
     int64_t cap = (T_cap + min_tokens - 1) / min_tokens;
@@ -364,7 +364,9 @@ kvq_status kvq_score(const kvq_codebook* cb, const int8_t* signs, const void* q,
   if (!scores || !aligned16(scores)) return fail(KVQ_ERR_INVALID_ARG, "scores NULL or not 16-byte aligned");
   p.seq_lens = seq_lens;
   p.scores = scores;
-  choose_splits(rs.units, T_cap, 0, &p.n_splits, &p.split_len);
+  // two score workgroups fit a compute unit (registers and LDS), and the second hides the first's prologue
+  // and memory latency
+  choose_splits(rs.units, T_cap, 0, &p.n_splits, &p.split_len, 2);
   const dim3 grid((unsigned)p.n_splits, (unsigned)rs.units);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (cb->kind == KVQ_HADAMARD_LM) return from_hip(kvq::launch_hlm_score(cb->d, cb->b, rs.gg, p, grid, s), "kvq_score");

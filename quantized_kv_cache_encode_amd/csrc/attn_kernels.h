@@ -1009,9 +1009,11 @@ void decode_kernel(const AttnParams p) {
   }
 }
 
-template <class S, int GG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void score_kernel(const AttnParams p) {
-  using Plan = LdsPlan<S, GG, kWaves, false>;
+template <class S, int GG, int NWV = kWaves>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV <= 8 ? 1 : NWV / 4, NWV <= 8 ? 2 : NWV / 4)))
+void score_kernel(const AttnParams p) {
+  constexpr int NT = 64 * NWV;
+  using Plan = LdsPlan<S, GG, NWV, false>;
   constexpr int HW = Plan::HW;
   __shared__ __align__(16) unsigned char smem[Plan::pst_off];
   float* lv = reinterpret_cast<float*>(smem + Plan::consts_off);
@@ -1033,7 +1035,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
                                               S::kNorm ? (int64_t)n_valid * 4 : 0);
 
   // codes and norms one chunk (of this wave) ahead, in two alternating register sets (as in decode_kernel)
-  constexpr int STR = kWaves * kChunk;
+  constexpr int STR = NWV * kChunk;
   uint32_t wa[S::NW], wb[S::NW];
   float na = 1.0f, nb = 1.0f;
   auto fetch = [&](int cc, uint32_t (&w)[S::NW], float& n) {
@@ -1060,8 +1062,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
     }
   };
   int c = wid * kChunk;
-  prologue<S, GG>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); });
-  S::template build<GG, HW>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); });
+  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
   lds_barrier();
 #pragma unroll
   for (int g = 0; g < GG; ++g)
