@@ -100,8 +100,10 @@ void kmeans_lloyd(const float* train, int64_t n, int dim, int stride, int K, int
 // Grid of equal cells over y in [-1, 1] for the encode kernel's threshold search: code(y) = (thresholds
 // in cells below y's cell) + (y >= the threshold inside y's cell, if any).  That is exact as long as no
 // cell holds two thresholds and no threshold lies within the rounding of y's cell index of a cell
-// boundary; the grid is chosen so that every threshold sits in [5%, 95%] of its cell, computed with the
-// same fp32 fused multiply-add the kernel uses.
+// boundary; the grid is chosen so that every threshold sits in [7%, 93%] of its cell, computed with the
+// same fp32 fused multiply-add the kernel uses.  The kernel finds y's cell through y * inv + shift + 2^20,
+// whose float spacing (1/8) moves it by at most 1/16 of a cell; the shift is a multiple of 1/8, so that
+// adding 2^20 to it is exact.
 bool choose_encode_cells(const float* t, int n, int* n_cells, float* cell_inv, float* cell_shift) {
   double min_gap = 1.0;
   for (int j = 0; j + 1 < n; ++j) min_gap = std::min(min_gap, (double)t[j + 1] - (double)t[j]);
@@ -111,14 +113,14 @@ bool choose_encode_cells(const float* t, int n, int* n_cells, float* cell_inv, f
     const int off = (int)std::ceil(1.0001 * (double)inv) + 1;
     const int cells = 2 * off + 1;
     if (cells > kEncodeMaxCells) return false;
-    for (int k = 0; k < 8; ++k) {
-      const float shift = (float)off + 0.5f + 0.0625f * (float)k;
+    for (int k = 0; k < 4; ++k) {
+      const float shift = (float)off + 0.5f + 0.125f * (float)k;  // a multiple of 1/8
       bool good = true;
       double prev_cell = -1e30;
       for (int j = 0; j < n && good; ++j) {
         const float v = std::fmaf(t[j], inv, shift);
         const double fr = (double)v - std::floor((double)v);
-        if (fr < 0.05 || fr > 0.95 || std::floor((double)v) == prev_cell) good = false;
+        if (fr < 0.07 || fr > 0.93 || std::floor((double)v) == prev_cell) good = false;
         prev_cell = std::floor((double)v);
       }
       if (good) {

@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void h
   constexpr int BPK = D * BITS / 8;    // code bytes per key
   constexpr int L = 1 << BITS;
   constexpr int ESZ = KF16 ? 2 : 4;
-  // per cell, 16 bytes apart: the threshold inside the cell (or +inf) and the count of thresholds below it
-  __shared__ float4 cells[kEncodeMaxCells];
+  // per cell, 8 bytes apart: the threshold inside the cell (or +inf) and the count of thresholds below it
+  __shared__ float2 cells[kEncodeMaxCells];
 
   // cell table: the count of thresholds in lower cells and the one threshold (if any) inside the cell
   for (int c = threadIdx.x; c < p.n_cells; c += 256) {
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void h
       below += cj < c ? 1 : 0;
       if (cj == c) inside = p.thresholds[j];
     }
-    cells[c] = make_float4(inside, __builtin_bit_cast(float, below), 0.0f, 0.0f);
+    cells[c] = make_float2(inside, __builtin_bit_cast(float, below));
   }
   __syncthreads();
 
@@ -50,17 +50,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void h
   const int lk = tid & (LPK - 1);
   float sg[kEncCpl];
   lane_signs<D>(p.signs, lk, sg);
-  // The cell's byte offset in the table comes straight from the bits of v = y * cell_inv + cell_shift + 2^19.
-  // In [2^19, 2^20) the spacing of floats is 1/16, so the mantissa holds 16 v rounded to the nearest
-  // sixteenth, and masking off its low four bits leaves 16 * cell.  The rounding moves v by at most 1/32 of
-  // a cell, and every threshold sits at least 5% of a cell inside its cell (choose_encode_cells), so where it
-  // moves v into the neighbouring cell no threshold lies in between and the count is the same.  The shift
-  // is a multiple of 1/16 below 2^18, so adding 2^19 to it is exact.  y is finite with |y| <= 1 up to
-  // rounding (keys with a non-finite coordinate do not get here), and the cells span |y| <= 1.0001 with a
-  // spare cell at either end, so v is positive and the cell is in range without a clamp.
-  const float shift19 = p.cell_shift + 0x1p19f;
+  // The cell's byte offset in the table comes straight from the bits of v = y * cell_inv + cell_shift + 2^20.
+  // In [2^20, 2^21) the spacing of floats is 1/8, so the mantissa holds 8 v rounded to the nearest eighth,
+  // and masking off its low three bits leaves 8 * cell.  The rounding moves v by at most 1/16 of a cell, and
+  // every threshold sits at least 7% of a cell inside its cell (choose_encode_cells), so where it moves v
+  // into the neighbouring cell no threshold lies in between and the count is the same.  The shift is a
+  // multiple of 1/8 below 2^18, so cell_shift + 2^20 is exact and the fma's single rounding is the only
+  // one.  y is finite with |y| <= 1 up to rounding (keys with a non-finite coordinate do not get here), and
+  // the cells span |y| <= 1.0001 with a spare cell at either end, so v is positive and the cell is in range
+  // without a clamp.
+  const float shift20 = p.cell_shift + 0x1p20f;
   auto code_of = [&](float y) -> uint32_t {
-    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(y, p.cell_inv, shift19)) & 0x7ffff0u;
+    const uint32_t off = __builtin_bit_cast(uint32_t, __builtin_fmaf(y, p.cell_inv, shift20)) & 0x7ffff8u;
     const float2 e = *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(cells) + off);
     return (uint32_t)__builtin_bit_cast(int, e.y) + (y >= e.x ? 1u : 0u);
   };

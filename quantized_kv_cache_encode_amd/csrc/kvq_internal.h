@@ -61,8 +61,8 @@ struct EncodeParams {
   float thresholds[15];
   uint32_t signs[8];
   // cell search of the Hadamard/Lloyd-Max encode: y (|y| <= 1) falls in cell floor(y * cell_inv +
-  // cell_shift) of n_cells; every threshold sits at least 5% of a cell away from a cell boundary and no
-  // cell holds two (choose_encode_cells)
+  // cell_shift) of n_cells; every threshold sits at least 7% of a cell away from a cell boundary, no cell
+  // holds two, and cell_shift is a multiple of 1/8 (choose_encode_cells)
   int n_cells;
   float cell_inv, cell_shift;
   int64_t key_begin, key_end;  // the keys [key_begin, key_end) of [B*Hkv*T_new] this launch encodes

@@ -322,10 +322,67 @@ static void check_select_signs() {
                           0.125f, errors, &best, ws, need, nullptr) != KVQ_OK);
 }
 
+// The encode kernel's cell search, replayed on the CPU with the same fp32 operations (fmaf rounds once, as
+// the GPU's fused multiply-add does): the cell table the kernel builds from the host's grid, then for y the
+// cell offset from the bits of fmaf(y, cell_inv, cell_shift + 2^20) masked to a multiple of 8, and the
+// count (thresholds below the cell) + (y >= the threshold inside it).  It must equal the plain count of
+// thresholds <= y for every y in [-1, 1]: checked at and around every threshold and every cell edge (the
+// neighbouring floats included) and on a fine sweep.
+static void check_cell_search() {
+  for (int d : {16, 32, 64, 128, 256})
+    for (int b = 1; b <= 4; ++b) {
+      kvq_codebook cb;
+      EXPECT(kvq_build_codebook(d, b, &cb) == KVQ_OK);
+      const int nt = (1 << b) - 1;
+      int n_cells = 0;
+      float inv = 0.0f, shift = 0.0f;
+      EXPECT(kvq::choose_encode_cells(cb.thresholds, nt, &n_cells, &inv, &shift));
+      if (n_cells <= 0) continue;
+      std::vector<float> inside(n_cells, INFINITY);
+      std::vector<uint32_t> below(n_cells, 0);
+      for (int c = 0; c < n_cells; ++c)
+        for (int j = 0; j < nt; ++j) {
+          const int cj = (int)std::floor(std::fmaf(cb.thresholds[j], inv, shift));
+          below[c] += cj < c ? 1u : 0u;
+          if (cj == c) inside[c] = cb.thresholds[j];
+        }
+      const float shift20 = shift + 0x1p20f;
+      EXPECT(shift20 - 0x1p20f == shift);  // exact
+      auto kernel_code = [&](float y) -> uint32_t {
+        uint32_t bits;
+        const float v = std::fmaf(y, inv, shift20);
+        std::memcpy(&bits, &v, 4);
+        const uint32_t c = (bits & 0x7ffff8u) / 8;
+        if (c >= (uint32_t)n_cells) return 999u;  // out of the table: a failure
+        return below[c] + (y >= inside[c] ? 1u : 0u);
+      };
+      auto plain_code = [&](float y) -> uint32_t {
+        uint32_t k = 0;
+        for (int j = 0; j < nt; ++j) k += (y >= cb.thresholds[j]) ? 1u : 0u;
+        return k;
+      };
+      int bad = 0;
+      auto probe = [&](float y) {
+        for (int s2 = -3; s2 <= 3; ++s2) {  // y and its three neighbouring floats either side
+          float z = y;
+          for (int i = 0; i < (s2 < 0 ? -s2 : s2); ++i) z = std::nextafter(z, s2 < 0 ? -2.0f : 2.0f);
+          if (z < -1.0f || z > 1.0f) continue;
+          if (kernel_code(z) != plain_code(z)) ++bad;
+        }
+      };
+      for (int j = 0; j < nt; ++j) probe(cb.thresholds[j]);
+      for (int c = 0; c <= n_cells; ++c) probe(((float)c - shift) / inv);  // near every cell edge
+      for (int i = 0; i <= 200000; ++i) probe(-1.0f + 2.0f * (float)i / 200000.0f);
+      probe(-0.0f);
+      EXPECT(bad == 0);
+    }
+}
+
 int main() {
   EXPECT(kvq_version() > 0);
   EXPECT(kvq_last_error() != nullptr);
   check_codebooks();
+  check_cell_search();
   check_encode();
   check_read_paths();
   check_select_signs();
