@@ -304,3 +304,26 @@ def test_pq_code_width(K):
     cb.K = 32  # 4-bit codes cannot index 32 centroids
     assert _call_encode(K, cb, None, norms=None) == K.KVQ_ERR_INVALID_ARG
     assert "code width" in K.kvq_last_error()
+
+
+def test_stream_read_validation(K):
+    """kvq_stream_read (the streaming-ceiling read) rejects bad arguments before launching."""
+    P = ctypes.c_void_p
+    lib = K._lib
+    sink = P(FAKE)
+
+    def call(codes=FAKE, norms=FAKE, v=FAKE, B=2, Hkv=2, T_cap=4096, d=64, bpk=32, n_splits=8):
+        return lib.kvq_stream_read(P(codes) if codes else None, P(norms) if norms else None, P(v) if v else None,
+                                   B, Hkv, T_cap, d, bpk, n_splits, sink, None)
+
+    assert call(codes=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(v=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(norms=FAKE + 4) == K.KVQ_ERR_INVALID_ARG          # misaligned
+    assert call(B=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(n_splits=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(n_splits=257) == K.KVQ_ERR_INVALID_ARG
+    assert call(B=300, Hkv=300) == K.KVQ_ERR_INVALID_ARG          # B*Hkv > 65535
+    assert call(T_cap=1 << 23) == K.KVQ_ERR_UNSUPPORTED            # 32-bit offsets
+    assert call(d=32, bpk=16) == K.KVQ_ERR_UNSUPPORTED             # instantiated for d = 64 and 128 only
+    assert call(d=64, bpk=24) == K.KVQ_ERR_UNSUPPORTED
+    assert "kvq_stream_read" in K.kvq_last_error()
