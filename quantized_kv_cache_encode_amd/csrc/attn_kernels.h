@@ -952,7 +952,9 @@ void decode_kernel(const AttnParams p) {
     }
   lds_barrier();
   const bool split_merge = p.n_splits > 1;
-  if (split_merge && tid == 0) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
+  // the arrival count is taken by the last thread, which has no element of the wave merge below when the
+  // workgroup has more threads than elements (12 waves at d = 64), so the two overlap
+  if (split_merge && tid == NT - 1) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
   for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
