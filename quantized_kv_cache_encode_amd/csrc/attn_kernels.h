@@ -736,6 +736,21 @@ void decode_kernel(const AttnParams p) {
       make_rsrc(app ? (const void*)(reinterpret_cast<const char*>(p.new_keys) + new_row * D * kesz) : p.codes,
                 app && wid == kEncWave ? D * kesz : 0);
 
+  // the lane's 16 coordinates of the new key (fp16 in the first 8 words): four 16-byte loads for fp32, two
+  // for fp16 (the rest read zeros), nonzero in the encoding lanes only; requested first, so that they have
+  // arrived when the encoding wave gets to them after the table is built
+  uint32_t kraw[kEncCpl];
+  if constexpr (S::kIntLut) {
+    if (app && wid == kEncWave) {
+      const int ko = lane * kEncCpl * kesz;
+#pragma unroll
+      for (int h = 0; h < kEncCpl / 4; ++h) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, kPol);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
+      }
+    }
+  }
   // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
   // burst streams in while the queries are rotated and the table is built.
   prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] {
@@ -748,16 +763,6 @@ void decode_kernel(const AttnParams p) {
   lds_barrier();
   if constexpr (S::kIntLut) {
     if (app && wid == kEncWave) {
-      // the lane's 16 coordinates of the new key (fp16 in the first 8 words): four 16-byte loads for fp32,
-      // two for fp16 (the rest read zeros), nonzero in the encoding lanes only
-      uint32_t kraw[kEncCpl];
-      const int ko = lane * kEncCpl * kesz;
-#pragma unroll
-      for (int h = 0; h < kEncCpl / 4; ++h) {
-        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 16 * h, 0, kPol);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kraw[4 * h + j] = r[j];
-      }
       if (enc_lanes) {
         float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
         uint64_t packed;
