@@ -58,9 +58,10 @@ def test_graph_replays_match_eager():
     assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "arrival counters not left at zero"
 
 
-@pytest.mark.parametrize("codec", ["pot", "pq4"])
+@pytest.mark.parametrize("codec", ["pot", "pq4", "pq8"])
 def test_graph_replays_match_eager_other_codecs(codec):
-    """The power-of-two and 4-bit PQ paths (encode of the step's key + decode) replayed from a graph."""
+    """The power-of-two, 4-bit PQ and byte-code PQ paths (encode of the step's key + decode) replayed from a
+    graph; the byte-code encode of one key runs the matrix-core kernel with one valid key in its workgroup."""
     import torch
     import quantized_kv_cache_encode_amd.kvq as K
 
@@ -69,7 +70,7 @@ def test_graph_replays_match_eager_other_codecs(codec):
         shape = W.scaled(W.LONGCTX, B=2, T=3000)
         cb = K.kvq_build_codebook_pot(shape.d, 4, 1)
     else:
-        shape = W.scaled(W.PQ4_GPT2_32X, B=2, T=2000)
+        shape = W.scaled(W.PQ4_GPT2_32X if codec == "pq4" else W.PQ_GPT2, B=2, T=2000)
         g0 = torch.Generator(device=dev)
         g0.manual_seed(4)
         cent = torch.randn((shape.Hkv, shape.m, shape.K, shape.d // shape.m), device=dev, generator=g0)
