@@ -52,6 +52,14 @@ constexpr int kMaxSplits = 256;        // T splits per (b, kv head, head group)
 constexpr int kRecPad = 4;             // split partial record = D accumulators + max + sum, padded to D + 4
 constexpr int kMergeTile = 8;          // splits whose partials the merging workgroup loads at once
 
+// ---- buffer-resource loads: 32-bit offsets from a per-split base, and every byte past the split's valid
+// range reads as 0, so the last (partial) chunk needs neither clamping nor branches.
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufFlags);
+}
+
 template <int B, int NW>
 __device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[NW], int i) {
   const int bit = i * B;
@@ -172,23 +180,45 @@ struct PqScorer {
   }
   __device__ static __forceinline__ float level_max(const float*) { return 1.0f; }
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).
+  // The centroids come in as 16-byte buffer loads of up to four entries at once, issued before any is used
+  // (behind a branch on c < K each entry's load would wait for the one before); a load past the head's
+  // centroids reads zeros, and entries with c >= K are set to zero after the loads.
   template <int GG, int HW, int NT = kThreads>
   __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
                                int tid) {
+    static_assert(DS % 4 == 0, "sub-vectors of whole 16-byte loads");
     constexpr int total = GG * ROWS * COLS;
+    constexpr int IT = (total + NT - 1) / NT;  // entries per thread
+    constexpr int BATCH = IT < 4 ? IT : 4;
     const int K = p.pq_K;
-    const float* cent = p.pq_cent + (size_t)kvh * M * K * DS;
-    for (int idx = tid; idx < total; idx += NT) {
-      const int hh = idx % HW;
-      const int c = (idx / HW) % COLS;
-      const int s = (idx / (HW * COLS)) % ROWS;
-      const int g = (idx / (HW * COLS * ROWS)) * HW + hh;
-      float acc = 0.0f;
-      if (c < K) {
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.pq_cent + (size_t)kvh * M * K * DS, (int64_t)M * K * DS * 4);
+    for (int i0 = 0; i0 < IT; i0 += BATCH) {
+      float cv[BATCH][DS];
 #pragma unroll
-        for (int k = 0; k < DS; ++k) acc += qs[g * D + s * DS + k] * cent[((size_t)s * K + c) * DS + k];
+      for (int b = 0; b < BATCH; ++b) {
+        const int idx = tid + (i0 + b) * NT;
+        const int c = (idx / HW) % COLS;
+        const int s = (idx / (HW * COLS)) % ROWS;
+#pragma unroll
+        for (int k4 = 0; k4 < DS / 4; ++k4) {
+          const float4_t v = __builtin_bit_cast(
+              float4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, ((s * K + c) * DS + 4 * k4) * 4, 0, 0));
+          cv[b][4 * k4 + 0] = v[0]; cv[b][4 * k4 + 1] = v[1]; cv[b][4 * k4 + 2] = v[2]; cv[b][4 * k4 + 3] = v[3];
+        }
       }
-      lut[idx] = acc;
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int idx = tid + (i0 + b) * NT;
+        if (i0 + b >= IT || idx >= total) continue;
+        const int hh = idx % HW;
+        const int c = (idx / HW) % COLS;
+        const int s = (idx / (HW * COLS)) % ROWS;
+        const int g = (idx / (HW * COLS * ROWS)) * HW + hh;
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < DS; ++k) acc += qs[g * D + s * DS + k] * cv[b][k];
+        lut[idx] = c < K ? acc : 0.0f;
+      }
     }
   }
 };
@@ -403,13 +433,6 @@ __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut
   }
 }
 
-// ---- buffer-resource loads: 32-bit offsets from a per-split base, and every byte past the split's valid
-// range reads as 0, so the last (partial) chunk needs neither clamping nor branches.
-constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data (gfx9 family)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufFlags);
-}
 
 // The N-byte code row at voff + soff into little-endian 32-bit words, loaded with cache policy POL.
 template <int N, int POL = 0>
