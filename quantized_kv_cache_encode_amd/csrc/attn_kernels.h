@@ -103,9 +103,16 @@ struct ScalarTable {
   // integer nearest to its value times 2^e_g, so the table of head g sums to at most 2^30 in magnitude along
   // any choice of one entry per row and integer sums never overflow.  One HW-wide entry (HW heads) per (head group, row,
   // column); each work item fills JPT consecutive columns of one (head group, row).
+  // nothing to request before the queries arrive
+  template <int GG, int NT>
+  struct Pre {};
+  template <int GG, int HW, int NT = kThreads>
+  __device__ static Pre<GG, NT> prefetch(const AttnParams&, int, int) {
+    return {};
+  }
   template <int GG, int HW, int NT = kThreads>
   __device__ static void build(const AttnParams&, const float* qs, const float* qa, const float* lv, float* lut,
-                               int, int tid) {
+                               int, int tid, const Pre<GG, NT>&) {
     using E = typename VecI<HW>::type;
     constexpr int JPT = COLS < 4 ? COLS : 4;
     constexpr int NJ = COLS / JPT;
@@ -182,29 +189,57 @@ struct PqScorer {
   // LUT[g][s][c] = q_{g,s} . C_{s,c}; columns c >= K are zero (never selected).
   // The centroids come in as 16-byte buffer loads of up to four entries at once, issued before any is used
   // (behind a branch on c < K each entry's load would wait for the one before); a load past the head's
-  // centroids reads zeros, and entries with c >= K are set to zero after the loads.
-  template <int GG, int HW, int NT = kThreads>
-  __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
-                               int tid) {
+  // centroids reads zeros, and entries with c >= K are set to zero after the loads.  The first batch is
+  // requested by prefetch, before the queries arrive (the centroids do not depend on them), except for
+  // 32-coordinate sub-vectors, whose batch would hold 128 registers through the query prologue.
+  template <int GG, int NT>
+  static constexpr int kIT = (GG * ROWS * COLS + NT - 1) / NT;  // entries per thread
+  template <int GG, int NT>
+  static constexpr int kBatch = kIT<GG, NT> < 4 ? kIT<GG, NT> : 4;
+  static constexpr bool kPrefetch = DS <= 16;
+  template <int GG, int NT>
+  struct Pre {
+    float cv[kPrefetch ? kBatch<GG, NT> : 1][DS];
+  };
+  template <int GG, int HW, int NT>
+  __device__ static void load_batch(const AttnParams& p, int kvh, int tid, int i0, float (&cv)[kBatch<GG, NT>][DS]) {
     static_assert(DS % 4 == 0, "sub-vectors of whole 16-byte loads");
-    constexpr int total = GG * ROWS * COLS;
-    constexpr int IT = (total + NT - 1) / NT;  // entries per thread
-    constexpr int BATCH = IT < 4 ? IT : 4;
     const int K = p.pq_K;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(p.pq_cent + (size_t)kvh * M * K * DS, (int64_t)M * K * DS * 4);
+#pragma unroll
+    for (int b = 0; b < kBatch<GG, NT>; ++b) {
+      const int idx = tid + (i0 + b) * NT;
+      const int c = (idx / HW) % COLS;
+      const int s = (idx / (HW * COLS)) % ROWS;
+#pragma unroll
+      for (int k4 = 0; k4 < DS / 4; ++k4) {
+        const float4_t v = __builtin_bit_cast(
+            float4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, ((s * K + c) * DS + 4 * k4) * 4, 0, 0));
+        cv[b][4 * k4 + 0] = v[0]; cv[b][4 * k4 + 1] = v[1]; cv[b][4 * k4 + 2] = v[2]; cv[b][4 * k4 + 3] = v[3];
+      }
+    }
+  }
+  template <int GG, int HW, int NT = kThreads>
+  __device__ static Pre<GG, NT> prefetch(const AttnParams& p, int kvh, int tid) {
+    Pre<GG, NT> pre;
+    if constexpr (kPrefetch) load_batch<GG, HW, NT>(p, kvh, tid, 0, pre.cv);
+    return pre;
+  }
+  template <int GG, int HW, int NT = kThreads>
+  __device__ static void build(const AttnParams& p, const float* qs, const float*, const float*, float* lut, int kvh,
+                               int tid, const Pre<GG, NT>& pre) {
+    constexpr int total = GG * ROWS * COLS;
+    constexpr int IT = kIT<GG, NT>, BATCH = kBatch<GG, NT>;
+    const int K = p.pq_K;
     for (int i0 = 0; i0 < IT; i0 += BATCH) {
       float cv[BATCH][DS];
+      if (kPrefetch && i0 == 0) {
 #pragma unroll
-      for (int b = 0; b < BATCH; ++b) {
-        const int idx = tid + (i0 + b) * NT;
-        const int c = (idx / HW) % COLS;
-        const int s = (idx / (HW * COLS)) % ROWS;
+        for (int b = 0; b < BATCH; ++b)
 #pragma unroll
-        for (int k4 = 0; k4 < DS / 4; ++k4) {
-          const float4_t v = __builtin_bit_cast(
-              float4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, ((s * K + c) * DS + 4 * k4) * 4, 0, 0));
-          cv[b][4 * k4 + 0] = v[0]; cv[b][4 * k4 + 1] = v[1]; cv[b][4 * k4 + 2] = v[2]; cv[b][4 * k4 + 3] = v[3];
-        }
+          for (int k = 0; k < DS; ++k) cv[b][k] = pre.cv[kPrefetch ? b : 0][k];
+      } else {
+        load_batch<GG, HW, NT>(p, kvh, tid, i0, cv);
       }
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
@@ -343,11 +378,23 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
       for (int j = 0; j < kEncCpl; ++j) qs[g * D + kEncCpl * k + j] = (x[j] * rs) * sc;
     }
   } else {
-    between();
-    for (int idx = tid; idx < GG * D; idx += NT) {
-      const size_t off = ((size_t)u.b * p.Hq + u.h0 + idx / D) * D + idx % D;
-      qs[idx] = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off] : reinterpret_cast<const float*>(p.q)[off];
+    // the queries first, then the caller's loads, so that waiting for the queries does not wait for those
+    constexpr int QPT = (GG * D + NT - 1) / NT;  // query elements per thread
+    float qv[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int idx = tid + j * NT;
+      const size_t off = ((size_t)u.b * p.Hq + u.h0 + (idx < GG * D ? idx : 0) / D) * D + idx % D;
+      qv[j] = idx >= GG * D ? 0.0f
+              : p.q_f16   ? (float)reinterpret_cast<const _Float16*>(p.q)[off]
+                          : reinterpret_cast<const float*>(p.q)[off];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j)
+      if (tid + j * NT < GG * D) qs[tid + j * NT] = qv[j];
   }
   lds_barrier();
 }
@@ -774,13 +821,15 @@ void decode_kernel(const AttnParams p) {
       }
     }
   }
-  // The first chunk's codes, norms and V are requested before the queries arrive, so that this first
-  // burst streams in while the queries are rotated and the table is built.
+  // What the table build can request before the queries arrive (the PQ centroids), then the first chunk's
+  // codes, norms and V, so that this first burst streams in while the queries are rotated and the table is
+  // built.
+  const auto pre = S::template prefetch<GG, HW, NT>(p, u.kvh, tid);
   prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] {
     fetch_codes(c, ka);
     fetch_v(c, ka);
   });
-  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
   if (lane == 0) s_prog.set(wid, 0);
   if (tid == 0) *s_newready = 0;
   lds_barrier();
@@ -1092,8 +1141,9 @@ void score_kernel(const AttnParams p) {
     }
   };
   int c = wid * kChunk;
+  const auto pre = S::template prefetch<GG, HW, NT>(p, u.kvh, tid);
   prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); });
-  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid);
+  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
   lds_barrier();
 #pragma unroll
   for (int g = 0; g < GG; ++g)
