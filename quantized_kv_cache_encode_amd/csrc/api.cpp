@@ -131,8 +131,13 @@ int device_cus() {
 // is all latency: there a split may hold half that, which halves each
 // workgroup's serial part, up to about half the compute units (beyond that,
 // and from one split to two, the merge costs more than the shorter splits
-// save).
-void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len, int per_cu = 1) {
+// save).  PQ decode (pq): every workgroup builds its head's whole table from the
+// K centroids of every subspace, so a split repeats that work; there a split keeps
+// at least four chunks per wave and the grid is not filled further (measured at
+// the GPT-2-like shape, 48 units: unsplit fastest for 1024 and 2048 tokens, two
+// splits for 4096).
+void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, int64_t* split_len, int per_cu = 1,
+                   bool pq = false) {
   const int64_t max_splits = (T_cap + 63) / 64;
   int64_t s;
   if (requested > 0) {
@@ -140,9 +145,9 @@ void choose_splits(int64_t units, int64_t T_cap, int requested, int* n_splits, i
   } else {
     const int64_t target = (int64_t)device_cus() * per_cu;
     s = (target + units - 1) / units;
-    const int64_t min_tokens = kvq::kReadThreads;  // 64 tokens for each of the workgroup's waves
+    const int64_t min_tokens = (pq ? 4 : 1) * kvq::kReadThreads;  // 64 tokens (pq: 256) per wave
     int64_t cap = (T_cap + min_tokens - 1) / min_tokens;
-    if (cap > 1 && units * cap < target / 2)
+    if (!pq && cap > 1 && units * cap < target / 2)
       cap = std::min((T_cap + min_tokens / 2 - 1) / (min_tokens / 2), (target / 2 + units - 1) / units);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
@@ -382,7 +387,7 @@ size_t kvq_decode_attn_workspace(const kvq_codebook* cb, int B, int Hq, int Hkv,
   const int64_t units = (int64_t)B * Hkv * (G / gg);
   int splits;
   int64_t len;
-  choose_splits(units, T_cap, n_splits, &splits, &len);
+  choose_splits(units, T_cap, n_splits, &splits, &len, 1, cb->kind == KVQ_PQ);
   return workspace_bytes(units, B, Hq, splits, cb->d);
 }
 
@@ -425,7 +430,7 @@ kvq_status decode_common(const char* name, const kvq_codebook* cb, const int8_t*
   p.out = out;
   p.out_f16 = odtype == KVQ_F16;
   p.zscale = scale * 1.4426950408889634f;
-  choose_splits(rs.units, T_cap, n_splits, &p.n_splits, &p.split_len);
+  choose_splits(rs.units, T_cap, n_splits, &p.n_splits, &p.split_len, 1, cb->kind == KVQ_PQ);
   if (p.n_splits > 1) {
     const size_t need = workspace_bytes(rs.units, B, Hq, p.n_splits, cb->d);
     if (!workspace || ws_bytes < need)

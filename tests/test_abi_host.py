@@ -189,6 +189,23 @@ def test_append_validation(K):
     assert "scalar codecs" in K.kvq_last_error()
 
 
+def test_pq_decode_split_rule(K):
+    """PQ decode splits the token axis less than the scalar codecs (every split rebuilds the head's whole
+    table): at least 2048 tokens per split and no extra splits to fill the device.  Checked through the
+    workspace query, which sizes the split merge for the same choice the launch makes (no workspace for one
+    split)."""
+    pq = K.kvq_codebook()
+    K._check(K._lib.kvq_codebook_pq(64, 8, 256, 12, ctypes.c_void_p(FAKE), ctypes.byref(pq)))
+    ws = lambda T, ns: K.kvq_decode_attn_workspace(pq, 4, 12, 12, T, ns)
+    assert ws(1024, 0) == ws(1024, 1) == 0
+    assert ws(2048, 0) == 0
+    assert ws(4096, 0) == ws(4096, 2) > 0
+    assert ws(1024, 4) > 0  # an explicit request still splits
+    # the Hadamard codec still splits a short cache over the device
+    hlm = K.kvq_build_codebook(128, 4)
+    assert K.kvq_decode_attn_workspace(hlm, 4, 32, 8, 1024, 0) > 0
+
+
 def test_offset_limit(K):
     """T_cap beyond the kernels' 32-bit offsets is rejected before any launch."""
     cb = K.kvq_build_codebook(256, 4)
