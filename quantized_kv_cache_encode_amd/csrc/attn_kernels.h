@@ -50,7 +50,7 @@ constexpr int kChunk = 64;
 constexpr float kLazyHeadroom = 8.0f;  // log2 of the largest probability allowed before rescaling
 constexpr int kMaxSplits = 256;        // T splits per (b, kv head, head group)
 constexpr int kRecPad = 4;             // split partial record = D accumulators + max + sum, padded to D + 4
-constexpr int kMergeTile = 8;          // splits whose partials the merging workgroup loads at once
+constexpr int kMergeTile = 16;         // splits whose partials the merging workgroup loads at once
 
 // ---- buffer-resource loads: 32-bit offsets from a per-split base, and every byte past the split's valid
 // range reads as 0, so the last (partial) chunk needs neither clamping nor branches.
