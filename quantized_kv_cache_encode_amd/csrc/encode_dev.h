@@ -349,12 +349,13 @@ __device__ __forceinline__ int64_t encode_row(const P& p, uint32_t gk) {
   return (int64_t)bh * p.T_cap + pos;
 }
 
-// Keys per workgroup of the encode kernels: contiguous ranges, whole passes, about 8192 workgroups for large
-// launches (a workgroup that streams its own range keeps the mix of key reads and code writes cheaper for the
-// memory than passes strided over the whole array) and one pass each for small ones.
+// Keys per workgroup of the encode kernels: contiguous ranges of whole pairs of passes (walk_keys runs its
+// passes in pairs, so a block of one pass would spend a second one on keys past its end), about 8192
+// workgroups for large launches (a workgroup that streams its own range keeps the mix of key reads and code
+// writes cheaper for the memory than passes strided over the whole array) and one pair each for small ones.
 inline int64_t encode_keys_per_block(int64_t n_keys, int kpb) {
   const int64_t per = (n_keys + 8191) / 8192;
-  return (per + kpb - 1) / kpb * kpb;
+  return (per + 2 * kpb - 1) / (2 * kpb) * (2 * kpb);
 }
 
 // Stores a lane's 16*BITS code bits at its byte offset lk*2*BITS of the key's code row (code rows are
