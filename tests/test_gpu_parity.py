@@ -505,15 +505,17 @@ def test_pq_score_and_decode_parity(K, oracle_mod, pq_case):
     tol = 1e-4 * np.linalg.norm(pq_case["q"].astype(np.float64), axis=-1)[:, :, None] * np.sqrt(khat_norm)
     assert np.all(np.abs(got - ref) <= tol)
     lens = [1024, 0, 513, 64]
-    out = K.kvq_decode_attn(cb, None, qd, codes, None, torch_dev(pq_case["v"]), scale=scale_of(sh.d),
-                            seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
-                            out_dtype=torch.float32).cpu().numpy()
     refo = oracle_mod.pq_decode_attn(cent64, pq_case["q"], pq_case["codes"], pq_case["v"], scale_of(sh.d),
                                      seq_lens=lens)
-    err = rel_l2_rows(out, refo)
-    log("  PQ decode max rel L2 %.3g" % float(err.max()))
-    assert np.all(err <= OUT_TOL)
-    assert np.all(out[1] == 0)
+    # the library's choice (one split at this length) and three splits (the split merge)
+    for ns in (0, 3):
+        out = K.kvq_decode_attn(cb, None, qd, codes, None, torch_dev(pq_case["v"]), scale=scale_of(sh.d),
+                                seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
+                                out_dtype=torch.float32, n_splits=ns).cpu().numpy()
+        err = rel_l2_rows(out, refo)
+        log("  PQ decode (n_splits %d) max rel L2 %.3g" % (ns, float(err.max())))
+        assert np.all(err <= OUT_TOL)
+        assert np.all(out[1] == 0)
 
 
 @pytest.fixture(scope="module", params=[W.PQ4_GPT2_32X, W.PQ4_GPT2_64X], ids=["pq4_32x", "pq4_64x"])
@@ -570,12 +572,13 @@ def test_pq4_score_and_decode_parity(K, oracle_mod, pq4_case):
     tol = 1e-4 * np.linalg.norm(pq4_case["q"].astype(np.float64), axis=-1)[:, :, None] * np.sqrt(khat_norm)
     assert np.all(np.abs(got - ref) <= tol)
     lens = [1024, 0, 700, 1]
-    out = K.kvq_decode_attn(cb, None, qd, codes, None, torch_dev(pq4_case["v"]), scale=scale_of(sh.d),
-                            seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
-                            out_dtype=torch.float32).cpu().numpy()
     refo = oracle_mod.pq_decode_attn(cent64, pq4_case["q"], pq4_case["codes"], pq4_case["v"], scale_of(sh.d),
                                      seq_lens=lens, bits=4)
-    err = rel_l2_rows(out, refo)
-    log("  4-bit PQ decode max rel L2 %.3g" % float(err.max()))
-    assert np.all(err <= OUT_TOL)
-    assert np.all(out[1] == 0)
+    for ns in (0, 2):  # the library's choice (one split) and two splits (the split merge)
+        out = K.kvq_decode_attn(cb, None, qd, codes, None, torch_dev(pq4_case["v"]), scale=scale_of(sh.d),
+                                seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda:0"),
+                                out_dtype=torch.float32, n_splits=ns).cpu().numpy()
+        err = rel_l2_rows(out, refo)
+        log("  4-bit PQ decode (n_splits %d) max rel L2 %.3g" % (ns, float(err.max())))
+        assert np.all(err <= OUT_TOL)
+        assert np.all(out[1] == 0)
