@@ -10,16 +10,17 @@
 // Shift-accumulate attention page (English abstract): decode attention fused
 // with an online softmax.
 //
-// Work decomposition (one workgroup = 8 waves of 64 lanes):
+// Work decomposition (one workgroup = 8 waves of 64 lanes, or 12 for d = 64 with fp16 V and long splits):
 //   workgroup <- (batch b, kv head, group of GG query heads, split of T);
-//   prologue: the GG queries are loaded into LDS, sign-flipped and put
-//   through an in-LDS fast Walsh-Hadamard transform (Hadamard codec), then
-//   the table for all GG heads is written to LDS as [GG/HW][rows][cols] of
-//   HW-wide float vectors (HW = min(GG, 4)), so one ds_read_b128 at
-//   (row, code) returns the entries of four heads;
-//   main loop: a wave takes 64 consecutive keys at a time, lane <-> key.
-//   The next chunk's codes and norms are fetched while the current one is
-//   scored, and the current chunk's V slices are fetched before its gathers.
+//   prologue: the GG queries are held 16 coordinates per lane (the write path's lane layout), sign-flipped
+//   and rotated with the write path's butterflies (in registers, then lane swizzles) for the Hadamard
+//   codec, scaled per head and stored in LDS; the table for all GG heads is then written to LDS as
+//   [GG/HW][rows][cols] vectors of HW heads (HW = min(GG, 4)): 32-bit fixed-point entries for the scalar
+//   codecs (each head at its own power-of-two scale), fp32 for PQ, so one ds_read_b128 at (row, code)
+//   returns the entries of four heads;
+//   main loop: a wave takes 64 keys at a time, lane <-> key.  The next chunk's codes and norms are
+//   fetched while the current one is scored; fp16 V slices are fetched one chunk ahead (8 waves, d <= 64)
+//   or when their chunk starts (12 waves, d = 128), and just before their products at d = 256.
 //   Every lane unpacks its key's codes from registers and gathers one vector
 //   per (row, head quad); all lanes read the same row at once and a row
 //   holds at most `cols` entries, so a wave's gather touches one contiguous
@@ -327,7 +328,56 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
 #pragma unroll
     for (int t = 0; t < 16; ++t) lv[t] = p.levels[t];
   }
-  if constexpr (S::kIntLut || S::kRotate) {
+  if constexpr ((S::kIntLut || S::kRotate) && D <= 64 && GG * D <= NT) {
+    // one coordinate per thread, a query's D threads within one wave: every butterfly stage is a lane
+    // exchange, so the rotation's chain is log2(D) exchanges instead of 16 coordinates' worth of in-register
+    // stages per lane; the sums and differences are those of the write path (signs folded into the first
+    // stage, the lower lane of a pair keeps x + partner and the upper one partner - x, as fused
+    // multiply-adds with +-1), so q' is the same to the bit
+    const int g = tid / D, i = tid % D;
+    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + i;
+    float x = 0.0f;
+    if (g < GG) x = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off] : reinterpret_cast<const float*>(p.q)[off];
+    __builtin_amdgcn_sched_barrier(0);
+    between();
+    __builtin_amdgcn_sched_barrier(0);
+    if (g < GG) {  // whole waves or aligned groups of D lanes, so the exchanges stay within the query
+      if constexpr (S::kRotate) {
+        // the sign words through wave-uniform (scalar) reads, then selected per lane
+        const uint32_t sw = (D > 32 && (i >> 5)) ? p.signs[D > 32 ? 1 : 0] : p.signs[0];
+        x *= ((sw >> (i & 31)) & 1u) ? -1.0f : 1.0f;  // exact
+        auto stage = [&](auto h_tag) {
+          constexpr int H = decltype(h_tag)::value;
+          float y;
+          if constexpr (H < 32) y = xor_lane<H>(x);
+          else y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tid ^ 32) << 2, __builtin_bit_cast(int, x)));
+          x = __builtin_fmaf(x, (i & H) ? -1.0f : 1.0f, y);
+        };
+        stage(std::integral_constant<int, 1>{});
+        stage(std::integral_constant<int, 2>{});
+        stage(std::integral_constant<int, 4>{});
+        stage(std::integral_constant<int, 8>{});
+        if constexpr (D >= 32) stage(std::integral_constant<int, 16>{});
+        if constexpr (D >= 64) stage(std::integral_constant<int, 32>{});
+      }
+      const float rs = S::kRotate ? 1.0f / __builtin_sqrtf((float)D) : 1.0f;
+      float sc = 1.0f;
+      if (qa != nullptr) {  // sum_i |q'_i| of the query: the bound that scales its fixed-point table
+        float a = fabsf(x);
+        a += xor_lane<1>(a);
+        a += xor_lane<2>(a);
+        a += xor_lane<4>(a);
+        a += xor_lane<8>(a);
+        if constexpr (D >= 32) a += xor_lane<16>(a);
+        if constexpr (D >= 64)
+          a += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tid ^ 32) << 2, __builtin_bit_cast(int, a)));
+        a *= rs;
+        if (i == 0) qa[g] = a;
+        sc = pow2f(fix_exp(a, S::level_max(p.levels)));
+      }
+      qs[g * D + i] = (x * rs) * sc;
+    }
+  } else if constexpr (S::kIntLut || S::kRotate) {
     constexpr int LPQ = EncLanes<D>::LPK;  // lanes per query (a power of two <= 16, so groups never straddle waves)
     static_assert(GG * LPQ <= NT, "one lane per 16 coordinates of every query");
     const int g = tid / LPQ, k = tid % LPQ;
