@@ -90,6 +90,11 @@ struct ScalarTable {
   static constexpr bool kNorm = true;
   static constexpr bool kNibbles = BITS * GRP == 4;  // rows indexed by the 4-bit fields of the packed codes
   static constexpr bool kIntLut = true;              // fixed-point table entries, summed exactly in 32-bit integers
+  static constexpr bool kRowPerCoord = GRP == 1;     // a table row holds one coordinate's entries
+  // where the query prologue writes the table itself (d <= 64, one coordinate per row) rows are padded by 16
+  // bytes: the lanes of a wave, each writing one row, then spread over the LDS banks instead of all landing
+  // on the same one
+  static constexpr int kRowPad = D <= 64 && GRP == 1 ? 16 : 0;
   // cache policy of the decode's streaming loads (codes, norms, values, new keys): non-temporal, since each
   // byte is read once per call and by a single load
   static constexpr int kLoadPolicy = kStreamLoad;
@@ -128,7 +133,7 @@ struct ScalarTable {
       for (int h = 0; h < HW; ++h)
 #pragma unroll
         for (int k = 0; k < GRP; ++k) qv[h][k] = qs[(g0 + h) * D + r * GRP + k];
-      E* row = L + (size_t)(e / NJ) * COLS + j0;
+      E* row = reinterpret_cast<E*>(reinterpret_cast<char*>(L) + (size_t)(e / NJ) * (COLS * sizeof(E) + kRowPad)) + j0;
 #pragma unroll
       for (int jj = 0; jj < JPT; ++jj) {
         const int n = j0 + jj;
@@ -181,6 +186,8 @@ struct PqScorer {
   static constexpr bool kNorm = false;
   static constexpr bool kNibbles = CB == 4;
   static constexpr bool kIntLut = false;
+  static constexpr bool kRowPerCoord = false;
+  static constexpr int kRowPad = 0;
   static constexpr int kLoadPolicy = 0;  // default policy: the non-temporal one measured slower on these small launches
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[NW], int i) {
     if constexpr (CB == 4) return (w[i >> 3] >> (4 * (i & 7))) & 15u;
@@ -268,7 +275,7 @@ struct LdsPlan {
   static constexpr int HW = GG < 4 ? GG : 4;
   static constexpr int NQ = GG / HW;
   static constexpr int RS = S::D + 4;
-  static constexpr size_t lut_bytes = (size_t)GG * S::ROWS * S::COLS * 4;
+  static constexpr size_t lut_bytes = (size_t)NQ * S::ROWS * (S::COLS * HW * 4 + S::kRowPad);
   static constexpr size_t lut_al = (lut_bytes + 15) / 16 * 16;
   static constexpr size_t red_bytes = kRec ? (size_t)NWV * GG * (RS + 2) * 4 + (size_t)GG * (S::D + 2) * 4 : 0;
   static constexpr bool kRedSeparate = kRec && lut_al + red_bytes + 48 * 1024 <= 160 * 1024;
@@ -319,8 +326,22 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 // `between` runs after this thread's query loads are issued and before they are used: the caller issues
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
-template <class S, int GG, int NT = kThreads, class F>
-__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between) {
+template <class S, int GG, int NT>
+constexpr bool lane_coord_prologue() {
+  return (S::kIntLut || S::kRotate) && S::D <= 64 && GG * S::D <= NT;
+}
+// With one coordinate per thread and one coordinate per table row (b = 3, 4), the thread of q'_{g,i} writes
+// head g's entries of row i itself: no pass through qs and no second barrier before the table is used.
+template <class S, int GG, int NT>
+constexpr bool direct_table() {
+  return lane_coord_prologue<S, GG, NT>() && S::kIntLut && S::kRowPerCoord;
+}
+
+// TABLE: the caller builds a scalar codec's lookup table from the prologue (the decode and score kernels);
+// where direct_table holds, the prologue writes it into `lut` and leaves qs unwritten.
+template <class S, int GG, int NT = kThreads, bool TABLE = false, class F>
+__device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* qa, float* lv, int tid, F&& between,
+                         void* lut = nullptr) {
   constexpr int D = S::D;
   // the levels come from the kernel arguments with wave-uniform (scalar) reads: indexed per lane they would be
   // a vector load from the argument segment whose wait would hold up everything issued after it
@@ -328,7 +349,7 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
 #pragma unroll
     for (int t = 0; t < 16; ++t) lv[t] = p.levels[t];
   }
-  if constexpr ((S::kIntLut || S::kRotate) && D <= 64 && GG * D <= NT) {
+  if constexpr (lane_coord_prologue<S, GG, NT>()) {
     // one coordinate per thread, a query's D threads within one wave: every butterfly stage is a lane
     // exchange, so the rotation's chain is log2(D) exchanges instead of 16 coordinates' worth of in-register
     // stages per lane; the sums and differences are those of the write path (signs folded into the first
@@ -375,7 +396,18 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
         if (i == 0) qa[g] = a;
         sc = pow2f(fix_exp(a, S::level_max(p.levels)));
       }
-      qs[g * D + i] = (x * rs) * sc;
+      const float qv = (x * rs) * sc;
+      if constexpr (TABLE && direct_table<S, GG, NT>()) {
+        // entry (row i, column n) of head g: component g % HW of the HW-wide vector at [g / HW][i][n]
+        // (the same products and rounding as the table build below)
+        constexpr int HW = GG < 4 ? GG : 4;
+        int* row = reinterpret_cast<int*>(reinterpret_cast<char*>(lut) +
+                                          ((g / HW) * S::ROWS + i) * (S::COLS * HW * 4 + S::kRowPad)) + g % HW;
+#pragma unroll
+        for (int n = 0; n < S::COLS; ++n) row[n * HW] = (int)__builtin_rintf(qv * p.levels[n]);
+      } else {
+        qs[g * D + i] = qv;
+      }
     }
   } else if constexpr (S::kIntLut || S::kRotate) {
     constexpr int LPQ = EncLanes<D>::LPK;  // lanes per query (a power of two <= 16, so groups never straddle waves)
@@ -508,7 +540,7 @@ __device__ __forceinline__ void lut_scores(const unsigned char* __restrict__ lut
       const uint32_t a = col_offset(i);
 #pragma unroll
       for (int qq = 0; qq < NQ; ++qq)
-        b[cc * NQ + qq] = *reinterpret_cast<const E*>(lut + (size_t)((qq * S::ROWS + i) * S::COLS) * ES + a);
+        b[cc * NQ + qq] = *reinterpret_cast<const E*>(lut + (size_t)(qq * S::ROWS + i) * (S::COLS * ES + S::kRowPad) + a);
     }
   };
   issue(0, buf[0]);
@@ -875,14 +907,16 @@ void decode_kernel(const AttnParams p) {
   // codes, norms and V, so that this first burst streams in while the queries are rotated and the table is
   // built.
   const auto pre = S::template prefetch<GG, HW, NT>(p, u.kvh, tid);
-  prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] {
-    fetch_codes(c, ka);
-    fetch_v(c, ka);
-  });
-  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
   if (lane == 0) s_prog.set(wid, 0);
   if (tid == 0) *s_newready = 0;
-  lds_barrier();
+  prologue<S, GG, NT, true>(p, u, qs, qa, lv, tid, [&] {
+    fetch_codes(c, ka);
+    fetch_v(c, ka);
+  }, smem);
+  if constexpr (!direct_table<S, GG, NT>()) {
+    S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
+    lds_barrier();
+  }
   if constexpr (S::kIntLut) {
     if (app && wid == kEncWave) {
       if (enc_lanes) {
@@ -1192,9 +1226,11 @@ void score_kernel(const AttnParams p) {
   };
   int c = wid * kChunk;
   const auto pre = S::template prefetch<GG, HW, NT>(p, u.kvh, tid);
-  prologue<S, GG, NT>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); });
-  S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
-  lds_barrier();
+  prologue<S, GG, NT, true>(p, u, qs, qa, lv, tid, [&] { fetch(c, wa, na); }, smem);
+  if constexpr (!direct_table<S, GG, NT>()) {
+    S::template build<GG, HW, NT>(p, qs, qa, lv, reinterpret_cast<float*>(smem), u.kvh, tid, pre);
+    lds_barrier();
+  }
 #pragma unroll
   for (int g = 0; g < GG; ++g)
     hs[g] = S::kIntLut ? pow2f(-fix_exp(qa[g], S::level_max(lv))) : 1.0f;
