@@ -91,10 +91,10 @@ struct ScalarTable {
   static constexpr bool kNibbles = BITS * GRP == 4;  // rows indexed by the 4-bit fields of the packed codes
   static constexpr bool kIntLut = true;              // fixed-point table entries, summed exactly in 32-bit integers
   static constexpr bool kRowPerCoord = GRP == 1;     // a table row holds one coordinate's entries
-  // where the query prologue writes the table itself (d <= 64, one coordinate per row) rows are padded by 16
+  // where the query prologue writes the table itself (d <= 128, one coordinate per row) rows are padded by 16
   // bytes: the lanes of a wave, each writing one row, then spread over the LDS banks instead of all landing
   // on the same one
-  static constexpr int kRowPad = D <= 64 && GRP == 1 ? 16 : 0;
+  static constexpr int kRowPad = D <= 128 && GRP == 1 ? 16 : 0;
   // cache policy of the decode's streaming loads (codes, norms, values, new keys): non-temporal, since each
   // byte is read once per call and by a single load
   static constexpr int kLoadPolicy = kStreamLoad;
@@ -326,12 +326,19 @@ __device__ __forceinline__ Unit decode_unit(const AttnParams& p, int GG) {
 // `between` runs after this thread's query loads are issued and before they are used: the caller issues
 // its first cache loads there, so they are in flight during the rotation and the table build (vector
 // memory loads complete in order, so waiting for the query does not wait for them).
+// Query layout of the read prologue for d <= 128: coordinate i of a query on lane i % 64 of its own wave
+// (for d < 64, d lanes of one wave), d / 64 coordinates per lane at d = 128.
+template <class S>
+struct LaneCoords {
+  static constexpr int LPQ = S::D < 64 ? S::D : 64;  // lanes per query
+  static constexpr int CPL = S::D / LPQ;             // coordinates per lane: i = l + 64 k
+};
 template <class S, int GG, int NT>
 constexpr bool lane_coord_prologue() {
-  return (S::kIntLut || S::kRotate) && S::D <= 64 && GG * S::D <= NT;
+  return (S::kIntLut || S::kRotate) && S::D <= 128 && GG * LaneCoords<S>::LPQ <= NT;
 }
-// With one coordinate per thread and one coordinate per table row (b = 3, 4), the thread of q'_{g,i} writes
-// head g's entries of row i itself: no pass through qs and no second barrier before the table is used.
+// With one coordinate per table row (b = 3, 4), the lane of q'_{g,i} writes head g's entries of row i itself:
+// no pass through qs and no second barrier before the table is used.
 template <class S, int GG, int NT>
 constexpr bool direct_table() {
   return lane_coord_prologue<S, GG, NT>() && S::kIntLut && S::kRowPerCoord;
@@ -350,29 +357,44 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
     for (int t = 0; t < 16; ++t) lv[t] = p.levels[t];
   }
   if constexpr (lane_coord_prologue<S, GG, NT>()) {
-    // one coordinate per thread, a query's D threads within one wave: every butterfly stage is a lane
-    // exchange, so the rotation's chain is log2(D) exchanges instead of 16 coordinates' worth of in-register
-    // stages per lane; the sums and differences are those of the write path (signs folded into the first
-    // stage, the lower lane of a pair keeps x + partner and the upper one partner - x, as fused
-    // multiply-adds with +-1), so q' is the same to the bit
-    const int g = tid / D, i = tid % D;
-    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + i;
-    float x = 0.0f;
-    if (g < GG) x = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off] : reinterpret_cast<const float*>(p.q)[off];
+    // Every butterfly stage of coordinate distance < 64 is a lane exchange and the one of distance 64
+    // (d = 128) is in registers, so the rotation's chain is log2(d) steps instead of 16 coordinates' worth of
+    // in-register stages per lane.  The stages run in the write path's order (distances 1, 2, 4, ...) with
+    // its sums and differences (signs folded into the first, the lower coordinate of a pair keeps x + partner
+    // and the upper one partner - x, as fused multiply-adds with +-1), so q' is the same to the bit.
+    constexpr int LPQ = LaneCoords<S>::LPQ, CPL = LaneCoords<S>::CPL;
+    const int g = tid / LPQ, l = tid % LPQ;
+    const size_t off = ((size_t)u.b * p.Hq + u.h0 + (g < GG ? g : 0)) * D + l;
+    float x[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      x[k] = 0.0f;
+      if (g < GG)
+        x[k] = p.q_f16 ? (float)reinterpret_cast<const _Float16*>(p.q)[off + 64 * k]
+                       : reinterpret_cast<const float*>(p.q)[off + 64 * k];
+    }
     __builtin_amdgcn_sched_barrier(0);
     between();
     __builtin_amdgcn_sched_barrier(0);
-    if (g < GG) {  // whole waves or aligned groups of D lanes, so the exchanges stay within the query
+    if (g < GG) {  // whole waves or aligned groups of d lanes, so the exchanges stay within the query
+      auto lane_xor = [&](float v, auto h_tag) -> float {
+        constexpr int H = decltype(h_tag)::value;
+        if constexpr (H < 32) return xor_lane<H>(v);
+        else return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tid ^ 32) << 2, __builtin_bit_cast(int, v)));
+      };
       if constexpr (S::kRotate) {
-        // the sign words through wave-uniform (scalar) reads, then selected per lane
-        const uint32_t sw = (D > 32 && (i >> 5)) ? p.signs[D > 32 ? 1 : 0] : p.signs[0];
-        x *= ((sw >> (i & 31)) & 1u) ? -1.0f : 1.0f;  // exact
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          // the sign words through wave-uniform (scalar) reads, then selected per lane: coordinate l + 64 k
+          // is bit l % 32 of word 2k + l / 32
+          const uint32_t sw = (D > 32 && (l >> 5)) ? p.signs[D > 32 ? 2 * k + 1 : 0] : p.signs[D > 32 ? 2 * k : 0];
+          x[k] *= ((sw >> (l & 31)) & 1u) ? -1.0f : 1.0f;  // exact
+        }
         auto stage = [&](auto h_tag) {
           constexpr int H = decltype(h_tag)::value;
-          float y;
-          if constexpr (H < 32) y = xor_lane<H>(x);
-          else y = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tid ^ 32) << 2, __builtin_bit_cast(int, x)));
-          x = __builtin_fmaf(x, (i & H) ? -1.0f : 1.0f, y);
+          const float s = (l & H) ? -1.0f : 1.0f;
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) x[k] = __builtin_fmaf(x[k], s, lane_xor(x[k], h_tag));
         };
         stage(std::integral_constant<int, 1>{});
         stage(std::integral_constant<int, 2>{});
@@ -380,33 +402,43 @@ __device__ void prologue(const AttnParams& p, const Unit& u, float* qs, float* q
         stage(std::integral_constant<int, 8>{});
         if constexpr (D >= 32) stage(std::integral_constant<int, 16>{});
         if constexpr (D >= 64) stage(std::integral_constant<int, 32>{});
+        if constexpr (CPL == 2) {  // distance 64: coordinate l keeps a + c, coordinate l + 64 gets a - c
+          const float a = x[0], c = x[1];
+          x[0] = a + c;
+          x[1] = a - c;
+        }
       }
       const float rs = S::kRotate ? 1.0f / __builtin_sqrtf((float)D) : 1.0f;
       float sc = 1.0f;
       if (qa != nullptr) {  // sum_i |q'_i| of the query: the bound that scales its fixed-point table
-        float a = fabsf(x);
-        a += xor_lane<1>(a);
-        a += xor_lane<2>(a);
-        a += xor_lane<4>(a);
-        a += xor_lane<8>(a);
-        if constexpr (D >= 32) a += xor_lane<16>(a);
-        if constexpr (D >= 64)
-          a += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((tid ^ 32) << 2, __builtin_bit_cast(int, a)));
+        float a = fabsf(x[0]);
+#pragma unroll
+        for (int k = 1; k < CPL; ++k) a += fabsf(x[k]);
+        a += lane_xor(a, std::integral_constant<int, 1>{});
+        a += lane_xor(a, std::integral_constant<int, 2>{});
+        a += lane_xor(a, std::integral_constant<int, 4>{});
+        a += lane_xor(a, std::integral_constant<int, 8>{});
+        if constexpr (D >= 32) a += lane_xor(a, std::integral_constant<int, 16>{});
+        if constexpr (D >= 64) a += lane_xor(a, std::integral_constant<int, 32>{});
         a *= rs;
-        if (i == 0) qa[g] = a;
+        if (l == 0) qa[g] = a;
         sc = pow2f(fix_exp(a, S::level_max(p.levels)));
       }
-      const float qv = (x * rs) * sc;
-      if constexpr (TABLE && direct_table<S, GG, NT>()) {
-        // entry (row i, column n) of head g: component g % HW of the HW-wide vector at [g / HW][i][n]
-        // (the same products and rounding as the table build below)
-        constexpr int HW = GG < 4 ? GG : 4;
-        int* row = reinterpret_cast<int*>(reinterpret_cast<char*>(lut) +
-                                          ((g / HW) * S::ROWS + i) * (S::COLS * HW * 4 + S::kRowPad)) + g % HW;
 #pragma unroll
-        for (int n = 0; n < S::COLS; ++n) row[n * HW] = (int)__builtin_rintf(qv * p.levels[n]);
-      } else {
-        qs[g * D + i] = qv;
+      for (int k = 0; k < CPL; ++k) {
+        const int i = l + 64 * k;
+        const float qv = (x[k] * rs) * sc;
+        if constexpr (TABLE && direct_table<S, GG, NT>()) {
+          // entry (row i, column n) of head g: component g % HW of the HW-wide vector at [g / HW][i][n]
+          // (the same products and rounding as the table build below)
+          constexpr int HW = GG < 4 ? GG : 4;
+          int* row = reinterpret_cast<int*>(reinterpret_cast<char*>(lut) +
+                                            ((g / HW) * S::ROWS + i) * (S::COLS * HW * 4 + S::kRowPad)) + g % HW;
+#pragma unroll
+          for (int n = 0; n < S::COLS; ++n) row[n * HW] = (int)__builtin_rintf(qv * p.levels[n]);
+        } else {
+          qs[g * D + i] = qv;
+        }
       }
     }
   } else if constexpr (S::kIntLut || S::kRotate) {
