@@ -721,11 +721,16 @@ __device__ __forceinline__ uint32_t await_word(const uint32_t* p, uint32_t w) {
   return w;
 }
 
-// Counts this workgroup in (one device-scope fetch-add, no retry loop) and tells whether it is the last of
-// the n_splits, which then merges them; the last one resets the counter for the next call.
-__device__ __forceinline__ bool elect_merger(unsigned* c, int n_splits) {
-  const unsigned t = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool last = t + 1u == (unsigned)n_splits;
+// Counts this workgroup in (one device-scope fetch-add, no retry loop) and returns the count before it.  The
+// caller requests it before the wave merge and reads it after (merger_from_count), so the round trip runs
+// under that merge.
+__device__ __forceinline__ unsigned count_arrival(unsigned* c) {
+  return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Whether the workgroup whose arrival found `before` others is the last of the n_splits, which then merges
+// them; the last one resets the counter for the next call.
+__device__ __forceinline__ bool merger_from_count(unsigned* c, unsigned before, int n_splits) {
+  const bool last = before + 1u == (unsigned)n_splits;
   if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return last;
 }
@@ -1145,9 +1150,8 @@ void decode_kernel(const AttnParams p) {
     }
   lds_barrier();
   const bool split_merge = p.n_splits > 1;
-  // the arrival count is taken by the last thread, which has no element of the wave merge below when the
-  // workgroup has more threads than elements (12 waves at d = 64), so the two overlap
-  if (split_merge && tid == NT - 1) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
+  unsigned arrived = 0u;  // the arrival count, requested here and read after the wave merge
+  if (split_merge && tid == NT - 1) arrived = count_arrival(p.counters + blockIdx.y);
   for (int idx = tid; idx < GG * D; idx += NT) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
@@ -1178,6 +1182,7 @@ void decode_kernel(const AttnParams p) {
   if (!split_merge) return;
 
   // ---- split merge: every workgroup but the last publishes its partials; the last merges all splits
+  if (tid == NT - 1) *s_flag = merger_from_count(p.counters + blockIdx.y, arrived, p.n_splits);
   lds_barrier();
   const bool last = *s_flag;
   uint32_t* wsw = reinterpret_cast<uint32_t*>(p.ws);

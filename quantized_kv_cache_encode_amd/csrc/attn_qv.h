@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))
   const bool split_merge = p.n_splits > 1;
   float* mine_m = qs;       // [GG] this workgroup's merged maxima and totals (the rotated queries are no
   float* mine_d = qs + GG;  // longer needed); its merged sums go to xs
-  if (split_merge && tid == 0) *s_flag = elect_merger(p.counters + blockIdx.y, p.n_splits);
+  if (split_merge && tid == 0) *s_flag = merger_from_count(p.counters + blockIdx.y, count_arrival(p.counters + blockIdx.y), p.n_splits);
   for (int idx = tid; idx < GG * D; idx += kThreads) {
     const int g = idx / D, dc = idx % D;
     float M = -INFINITY;
