@@ -187,6 +187,11 @@ SCORE_CASES = [
     ("d32_b3_G1", W.scaled(W.LLAMA8B, d=32, b=3, Hq=3, Hkv=3, T=129), None, None, None),
     ("d64_G6", W.scaled(W.LONGCTX, B=1, Hq=12, Hkv=2, T=300), None, None, None),
     ("d128_G16", W.scaled(W.LLAMA8B, Hq=32, Hkv=2, T=200), None, None, None),
+    # query layouts of the read prologue below one wave per query (16 and 32 lanes per query), with the table
+    # rows written by the prologue (b = 3, 4) at one, two and four heads per table entry
+    ("d16_b4_G4", W.scaled(W.TINY, b=4, B=2, Hq=8, Hkv=2, T=150), None, None, None),
+    ("d32_b4_G8", W.scaled(W.LLAMA8B, d=32, b=4, B=2, Hq=16, Hkv=2, T=260), None, None, None),
+    ("d32_b3_G2", W.scaled(W.LLAMA8B, d=32, b=3, B=1, Hq=4, Hkv=2, T=130), None, None, None),
 ]
 
 
@@ -258,6 +263,9 @@ DECODE_CASES = [
     ("d32_b1_G1_fp32v", W.scaled(W.TINY, d=32, b=1, B=2, Hq=2, Hkv=2, T=333), None, None, None, 0, "f32"),
     ("d64_G6", W.scaled(W.LONGCTX, B=1, Hq=12, Hkv=2, T=600), None, None, None, 0, "f16"),
     ("d128_G16", W.scaled(W.LLAMA8B, Hq=32, Hkv=2, T=300), None, None, None, 0, "f32"),
+    ("d16_b4_G4", W.scaled(W.TINY, b=4, B=2, Hq=8, Hkv=2, T=150), None, None, None, 2, "f16"),
+    ("d32_b4_G8", W.scaled(W.LLAMA8B, d=32, b=4, B=2, Hq=16, Hkv=2, T=260), None, None, [260, 77], 0, "f16"),
+    ("d32_b3_G2_fp32v", W.scaled(W.TINY, d=32, b=3, B=1, Hq=4, Hkv=2, T=130), None, None, None, 0, "f32"),
 ]
 
 
