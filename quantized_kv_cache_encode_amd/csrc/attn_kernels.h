@@ -956,7 +956,57 @@ void decode_kernel(const AttnParams p) {
   }
   if constexpr (S::kIntLut) {
     if (app && wid == kEncWave) {
-      if (enc_lanes) {
+      // 4-bit Hadamard codes: the key's D/16 lanes rotate and scale it as the encode kernel does, then the
+      // whole wave counts thresholds (each lane one coordinate per 64) and packs the codes with lane exchanges,
+      // instead of 16 coordinates' 15 comparisons each on D/16 lanes; same comparisons, same codes.  Keys with
+      // a non-finite sum of squares take the write path's own route below.
+      bool fast = false;
+      if constexpr (S::kRotate && S::CODE_BITS == 4) {
+        float x[kEncCpl];
+        float nrm = 0.0f;
+        bool fin = false;
+        if (enc_lanes) {
+          if (p.new_f16) key_lane_floats<true>(kraw, x);
+          else key_lane_floats<false>(kraw, x);
+          float sg[kEncCpl];
+          lane_signs<D>(p.signs, lane, sg);
+          const float ss = rotate_key_lane<D>(x, lane, sg);
+          const float inv = unit_scale_ss<D>(ss, nrm);
+          fin = ss <= 0x1.fffffep127f;
+          if (fin) unit_vector(x, inv);
+        }
+        fast = __builtin_amdgcn_readfirstlane(fin ? 1 : 0) != 0;  // lane 0 holds the key
+        if (fast) {
+          float* ys = qs;  // the queries' staging area is free once the table is built: D floats
+          if (enc_lanes) {
+#pragma unroll
+            for (int h = 0; h < kEncCpl / 4; ++h)
+              *reinterpret_cast<float4*>(ys + kEncCpl * lane + 4 * h) = make_float4(x[4 * h], x[4 * h + 1], x[4 * h + 2], x[4 * h + 3]);
+          }
+          wave_lds_sync();
+          const bool row_writer = blockIdx.y % p.n_groups == 0;  // one cache writer per (b, kv head)
+          const int64_t row = new_row * p.T_cap + (u.len - 1);
+#pragma unroll
+          for (int k0 = 0; k0 < D; k0 += 64) {
+            const int i = k0 + lane;
+            uint32_t w = 0;
+            if (i < D) w = code_by_count<4>(ys[i], p.thresholds);
+            // eight consecutive coordinates' nibbles into one word, LSB first, in lane 8m of each group
+            w |= __builtin_bit_cast(uint32_t, xor_lane<1>(__builtin_bit_cast(float, w))) << 4;
+            w |= __builtin_bit_cast(uint32_t, xor_lane<2>(__builtin_bit_cast(float, w))) << 8;
+            w |= __builtin_bit_cast(uint32_t, xor_lane<4>(__builtin_bit_cast(float, w))) << 16;
+            if (i < D && (lane & 7) == 0) {
+              s_newc[i / 8] = w;
+              if (row_writer) reinterpret_cast<uint32_t*>(p.app_codes + row * S::BPK)[i / 8] = w;
+            }
+          }
+          if (lane == 0) {
+            *s_newn = nrm;
+            if (row_writer) p.app_norms[row] = nrm;
+          }
+        }
+      }
+      if (enc_lanes && !fast) {
         float nrm;  // the key's norm (Hadamard codec) or max |k_i| (power-of-two codec)
         uint64_t packed;
         if constexpr (S::kRotate) {
