@@ -956,12 +956,14 @@ void decode_kernel(const AttnParams p) {
   }
   if constexpr (S::kIntLut) {
     if (app && wid == kEncWave) {
-      // 4-bit Hadamard codes: the key's D/16 lanes rotate and scale it as the encode kernel does, then the
-      // whole wave counts thresholds (each lane one coordinate per 64) and packs the codes with lane exchanges,
-      // instead of 16 coordinates' 15 comparisons each on D/16 lanes; same comparisons, same codes.  Keys with
-      // a non-finite sum of squares take the write path's own route below.
+      // Hadamard codes of 1, 2 or 4 bits: the key's D/16 lanes rotate and scale it as the encode kernel does,
+      // then the whole wave counts thresholds (each lane one coordinate per 64) and packs the codes with lane
+      // exchanges, instead of 16 coordinates' comparisons with every threshold on D/16 lanes; same
+      // comparisons, same codes.  3-bit codes (which straddle words), rows shorter than a word (d = 16, 1 bit)
+      // and keys with a non-finite sum of squares take the write path's own route below.
+      constexpr int CB = S::CODE_BITS;
       bool fast = false;
-      if constexpr (S::kRotate && S::CODE_BITS == 4) {
+      if constexpr (S::kRotate && (CB == 1 || CB == 2 || CB == 4) && (D * CB) % 32 == 0) {  // whole words
         float x[kEncCpl];
         float nrm = 0.0f;
         bool fin = false;
@@ -989,15 +991,22 @@ void decode_kernel(const AttnParams p) {
 #pragma unroll
           for (int k0 = 0; k0 < D; k0 += 64) {
             const int i = k0 + lane;
+            constexpr int CPW = 32 / CB;  // coordinates per 32-bit word of the code row
             uint32_t w = 0;
-            if (i < D) w = code_by_count<4>(ys[i], p.thresholds);
-            // eight consecutive coordinates' nibbles into one word, LSB first, in lane 8m of each group
-            w |= __builtin_bit_cast(uint32_t, xor_lane<1>(__builtin_bit_cast(float, w))) << 4;
-            w |= __builtin_bit_cast(uint32_t, xor_lane<2>(__builtin_bit_cast(float, w))) << 8;
-            w |= __builtin_bit_cast(uint32_t, xor_lane<4>(__builtin_bit_cast(float, w))) << 16;
-            if (i < D && (lane & 7) == 0) {
-              s_newc[i / 8] = w;
-              if (row_writer) reinterpret_cast<uint32_t*>(p.app_codes + row * S::BPK)[i / 8] = w;
+            if (i < D) w = code_by_count<CB>(ys[i], p.thresholds);
+            // CPW consecutive coordinates' codes into one word, LSB first, in lane CPW m of each group
+            auto merge = [&](auto dl_tag) {
+              constexpr int DL = decltype(dl_tag)::value;
+              if constexpr (DL < CPW) w |= __builtin_bit_cast(uint32_t, xor_lane<DL>(__builtin_bit_cast(float, w))) << (CB * DL);
+            };
+            merge(std::integral_constant<int, 1>{});
+            merge(std::integral_constant<int, 2>{});
+            merge(std::integral_constant<int, 4>{});
+            merge(std::integral_constant<int, 8>{});
+            merge(std::integral_constant<int, 16>{});
+            if (i < D && (lane & (CPW - 1)) == 0) {
+              s_newc[i / CPW] = w;
+              if (row_writer) reinterpret_cast<uint32_t*>(p.app_codes + row * S::BPK)[i / CPW] = w;
             }
           }
           if (lane == 0) {

@@ -36,6 +36,10 @@ CASES = [
     ("d64_G6_two_groups", W.scaled(W.LONGCTX, B=2, Hq=12, Hkv=2, T=600), None, None, [600, 333], 0, "f16"),
     ("d256_b3", W.scaled(W.LONGCTX, d=256, b=3, B=2, Hq=4, Hkv=2, T=300), None, None, [300, 129], 0, "f16"),
     ("d32_b1_G1", W.scaled(W.TINY, d=32, b=1, B=2, Hq=2, Hkv=2, T=200, dtype="f16"), None, None, None, 0, "f16"),
+    # the new key's codes packed by the whole wave (rows of whole words), and a row shorter than a word
+    ("d16_b4_G4", W.scaled(W.TINY, b=4, B=2, Hq=8, Hkv=2, T=150), None, None, [150, 3], 0, "f32"),
+    ("d128_b1_G4", W.scaled(W.LLAMA8B, b=1, B=2, T=700), None, None, [700, 65], 0, "f16"),
+    ("d16_b1_short_row", W.scaled(W.TINY, b=1, B=2, Hq=2, Hkv=2, T=90), None, None, None, 0, "f32"),
     # splits of 4096 tokens: 12-wave workgroups
     ("longctx_long_splits", W.LONGCTX, [0, 5], 8192, [8192, 6001], 2, "f16"),
 ]
