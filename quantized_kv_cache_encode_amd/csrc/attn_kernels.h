@@ -12,12 +12,14 @@
 //
 // Work decomposition (one workgroup = 8 waves of 64 lanes, or 12 for d = 64 with fp16 V and long splits):
 //   workgroup <- (batch b, kv head, group of GG query heads, split of T);
-//   prologue: the GG queries are held 16 coordinates per lane (the write path's lane layout), sign-flipped
-//   and rotated with the write path's butterflies (in registers, then lane swizzles) for the Hadamard
-//   codec, scaled per head and stored in LDS; the table for all GG heads is then written to LDS as
+//   prologue: each of the GG queries is held by one wave for d <= 128 (coordinate i on lane i % 64), else
+//   16 coordinates per lane as in the write path; for the Hadamard codec it is sign-flipped and rotated
+//   with the write path's sums and differences (lane exchanges, and in-register stages where a lane holds
+//   several coordinates) and scaled per head; the table for all GG heads is in LDS as
 //   [GG/HW][rows][cols] vectors of HW heads (HW = min(GG, 4)): 32-bit fixed-point entries for the scalar
 //   codecs (each head at its own power-of-two scale), fp32 for PQ, so one ds_read_b128 at (row, code)
-//   returns the entries of four heads;
+//   returns the entries of four heads.  Where a row holds one coordinate, the lanes of the prologue write
+//   the rows themselves; otherwise q' goes through LDS to a separate table build;
 //   main loop: a wave takes 64 keys at a time, lane <-> key.  The next chunk's codes and norms are
 //   fetched while the current one is scored; fp16 V slices are fetched one chunk ahead (8 waves, d <= 64)
 //   or when their chunk starts (12 waves, d = 128), and just before their products at d = 256.
