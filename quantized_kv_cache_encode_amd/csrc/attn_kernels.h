@@ -958,14 +958,15 @@ void decode_kernel(const AttnParams p) {
   }
   if constexpr (S::kIntLut) {
     if (app && wid == kEncWave) {
-      // Hadamard codes of 1, 2 or 4 bits: the key's D/16 lanes rotate and scale it as the encode kernel does,
-      // then the whole wave counts thresholds (each lane one coordinate per 64) and packs the codes with lane
-      // exchanges, instead of 16 coordinates' comparisons with every threshold on D/16 lanes; same
-      // comparisons, same codes.  3-bit codes (which straddle words), rows shorter than a word (d = 16, 1 bit)
-      // and keys with a non-finite sum of squares take the write path's own route below.
+      // Hadamard codes: the key's D/16 lanes rotate and scale it as the encode kernel does, then the whole wave
+      // counts thresholds (each lane one coordinate per 64) instead of 16 coordinates' comparisons with every
+      // threshold on D/16 lanes; same comparisons, same codes.  Codes of 1, 2 or 4 bits in rows of whole
+      // words are packed with lane exchanges, the others by the key's lanes.  Keys with a non-finite sum of
+      // squares take the write path's own route below.
       constexpr int CB = S::CODE_BITS;
       bool fast = false;
-      if constexpr (S::kRotate && (CB == 1 || CB == 2 || CB == 4) && (D * CB) % 32 == 0) {  // whole words
+      constexpr bool kWords = (CB == 1 || CB == 2 || CB == 4) && (D * CB) % 32 == 0;  // rows of whole words
+      if constexpr (S::kRotate) {
         float x[kEncCpl];
         float nrm = 0.0f;
         bool fin = false;
@@ -990,8 +991,34 @@ void decode_kernel(const AttnParams p) {
           wave_lds_sync();
           const bool row_writer = blockIdx.y % p.n_groups == 0;  // one cache writer per (b, kv head)
           const int64_t row = new_row * p.T_cap + (u.len - 1);
+          if constexpr (!kWords) {
+            // other rows: the codes go back to the key's lanes as bytes over the coordinates just read, and
+            // are packed there as in the write path
+            constexpr int NCI = (D + 63) / 64;
+            uint32_t cv[NCI];
 #pragma unroll
-          for (int k0 = 0; k0 < D; k0 += 64) {
+            for (int k = 0; k < NCI; ++k) {
+              const int i = 64 * k + lane;
+              cv[k] = i < D ? code_by_count<CB>(ys[i], p.thresholds) : 0u;
+            }
+            wave_lds_sync();  // every lane has read its coordinates before the bytes overwrite them
+            uint8_t* cb8 = reinterpret_cast<uint8_t*>(ys);
+#pragma unroll
+            for (int k = 0; k < NCI; ++k)
+              if (64 * k + lane < D) cb8[64 * k + lane] = (uint8_t)cv[k];
+            wave_lds_sync();
+            if (enc_lanes) {
+              const uint4 q4 = *reinterpret_cast<const uint4*>(cb8 + kEncCpl * lane);
+              const uint32_t wd[4] = {q4.x, q4.y, q4.z, q4.w};
+              uint64_t packed = 0;
+#pragma unroll
+              for (int j = 0; j < kEncCpl; ++j) packed |= (uint64_t)((wd[j / 4] >> (8 * (j % 4))) & 0xffu) << (CB * j);
+              store_code_bits<CB>(reinterpret_cast<uint8_t*>(s_newc), lane, packed);
+              if (row_writer) store_code_bits<CB>(p.app_codes + row * S::BPK, lane, packed);
+            }
+          }
+#pragma unroll
+          for (int k0 = 0; k0 < (kWords ? D : 0); k0 += 64) {
             const int i = k0 + lane;
             constexpr int CPW = 32 / CB;  // coordinates per 32-bit word of the code row
             uint32_t w = 0;
